@@ -1,0 +1,266 @@
+"""Benchmark of the BitLinear W1.58A8 hot path on one MI355X.
+
+Default workload: the 2B-class decode step, one token through a 2560 -> 6912
+BitLinear and the 6912 -> 2560 down-projection (ternary weights, 2-bit
+packed; int8 per-token activations).  One step = per-token quantisation of
+the input, the up GEMV with fused dequant, quantisation of the down input,
+the down GEMV with fused dequant.  Weights are packed once before timing (the
+pages describe packing as a one-time conversion).  The timed steps rotate
+over enough distinct copies of the packed weights (> 512 MB) that they
+stream from HBM, not from the 256 MB last-level cache.
+
+value = packed-weight bytes of both projections per step / wall time per
+step (GB/s), launch gaps and the quantisation kernels included.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-extra]
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("BitLinear W1.58A8: decode GEMV weight GB/s (% HBM peak); "
+          "prefill int8 TOPS (% MFMA)")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA (5.0 POPS)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def event_time_per_launch(fn, n, torch):
+    """Average duration of fn()'s kernel, from an event pair around each launch
+    on the current stream (the one the binding launches on)."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(ms)), float(np.median(ms))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: only one GPU is supported in this build (asked for {args.gpus}); "
+              "the multi-GPU split is a design note, not a measured path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ternary_weight_linear_ternarize_amd import binding as B
+    from ternary_weight_linear_ternarize_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    # ---------------- setup (untimed): inputs, one-time packing, copies
+    c = synth.DECODE_2B
+    K, N = c["K"], c["N"]
+    d = synth.decode_2b()
+    Wup, sup = B.bitlinear_pack(torch.from_numpy(d["W_up"]).to(dev))
+    Wdn, sdn = B.bitlinear_pack(torch.from_numpy(d["W_down"]).to(dev))
+    x = torch.from_numpy(d["x"]).to(dev)
+    xd = torch.from_numpy(d["x_d"]).to(dev)
+    pbytes = Wup.numel() * 4
+    copies = max(2, int(np.ceil(600e6 / (2 * pbytes))))
+    ups = [Wup.clone() for _ in range(copies)]
+    dns = [Wdn.clone() for _ in range(copies)]
+    q1 = B.bitlinear_quant_act(x)
+    q2 = B.bitlinear_quant_act(xd)
+    y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+    y2 = torch.empty((1, K), dtype=torch.float32, device=dev)
+
+    def step(i):
+        j = i % copies
+        B.bitlinear_quant_act(x, out=q1)
+        B.bitlinear_forward(q1[0], q1[1], q1[2], K, ups[j], sup, N, out=y1)
+        B.bitlinear_quant_act(xd, out=q2)
+        B.bitlinear_forward(q2[0], q2[1], q2[2], N, dns[j], sdn, K, out=y2)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    step_bytes = 2 * pbytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # ---------------- dominant kernel: the up GEMV, per-launch event timing
+    nl = 400
+    up_ms, up_med = event_time_per_launch(
+        lambda i: B.bitlinear_forward(q1[0], q1[1], q1[2], K, ups[i % copies], sup, N, out=y1),
+        nl, torch)
+    alg_up = pbytes + K + 4 + 4 + 4 + N * 4   # W + xq + x_scale + rowsum + w_scale + y
+    dn_ms, dn_med = event_time_per_launch(
+        lambda i: B.bitlinear_forward(q2[0], q2[1], q2[2], N, dns[i % copies], sdn, K, out=y2),
+        nl, torch)
+    alg_dn = pbytes + N + 12 + K * 4
+    achieved = alg_up / (up_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemv_kernel<1,4,0> (2560->6912, M=1)",
+                "avg_us": round(up_ms * 1e3, 3), "median_us": round(up_med * 1e3, 3),
+                "algorithmic_bytes": alg_up}
+    kernels = {
+        "gemv_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3), "GBps": round(achieved, 1)},
+        "gemv_down_6912x2560": {"avg_us": round(dn_ms * 1e3, 3),
+                                "GBps": round(alg_dn / (dn_ms * 1e-3) / 1e9, 1)},
+    }
+    del ups, dns
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        kernels.update(extra_workloads(torch, B, synth, dev))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, args.cpu_seconds, step_bytes)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "decode 2B-class: M=1, BitLinear 2560->6912 + 6912->2560, "
+                               "ternary 2-bit packed weights ~N(0,0.02), x ~N(0,1) int8 per token",
+                   "M": 1, "K": K, "N": N, "weight_copies": copies,
+                   "step_weight_bytes": step_bytes, "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def extra_workloads(torch, B, synth, dev):
+    """Kernel timings of the other shapes (prefill GEMM, 100B-class decode, FFN)."""
+    res = {}
+    # prefill GEMM: M=2048, K=2560, N=6912
+    c = synth.PREFILL_2B
+    M, K, N = c["M"], c["K"], c["N"]
+    p = synth.prefill_2b()
+    Wp, sc = B.bitlinear_pack(torch.from_numpy(p["W"]).to(dev))
+    X = torch.from_numpy(p["X"]).to(dev)
+    q = B.bitlinear_quant_act(X)
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    copies = [Wp.clone() for _ in range(4)]
+    for i in range(5):
+        B.bitlinear_forward(q[0], q[1], q[2], K, copies[i % 4], sc, N, out=Y)
+    ms, med = event_time_per_launch(
+        lambda i: B.bitlinear_forward(q[0], q[1], q[2], K, copies[i % 4], sc, N, out=Y), 50, torch)
+    ops = 2.0 * M * N * K
+    res["prefill_gemm_2048x2560x6912"] = {
+        "avg_us": round(ms * 1e3, 2), "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+        "frac_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+    qa_ms, _ = event_time_per_launch(lambda i: B.bitlinear_quant_act(X, out=q), 20, torch)
+    res["act_quant_2048x2560"] = {"avg_us": round(qa_ms * 1e3, 2),
+                                  "GBps": round(M * K * 5 / (qa_ms * 1e-3) / 1e9, 1)}
+    del copies, Y, X, q, Wp
+    torch.cuda.empty_cache()
+
+    # 100B-class decode: K=8192, N=28672, M in {1, 8}
+    c = synth.DECODE_100B
+    K, N = c["K"], c["N"]
+    p = synth.decode_100b()
+    Wd = torch.from_numpy(p["W"]).to(dev)
+    del p["W"]
+    for mode, tag in ((B.BL_TERNARY, "ternary"), (B.BL_BINARY, "binary")):
+        Wp, sc = B.bitlinear_pack(Wd, mode)
+        pb = Wp.numel() * 4
+        ncp = max(2, int(np.ceil(600e6 / pb)))
+        cps = [Wp.clone() for _ in range(ncp)]
+        for M in (1, 8):
+            q = B.bitlinear_quant_act(torch.from_numpy(p["X"][:M]).to(dev))
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            for i in range(3):
+                B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y)
+            ms, med = event_time_per_launch(
+                lambda i: B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y),
+                60, torch)
+            alg = pb + M * (K + 8) + 4 + M * N * 4
+            res[f"decode_100b_{tag}_M{M}"] = {
+                "avg_us": round(ms * 1e3, 2), "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+                "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del cps, Wp
+        torch.cuda.empty_cache()
+    del Wd
+    torch.cuda.empty_cache()
+
+    # FFN block: D=2560, F=6912, M in {1, 8, 64}
+    c = synth.FFN_2B
+    D, F = c["D"], c["F"]
+    f = synth.ffn_2b()
+    packs = [B.bitlinear_pack(torch.from_numpy(f[n]).to(dev)) for n in ("W_gate", "W_up", "W_down")]
+    wbytes = sum(pk[0].numel() * 4 for pk in packs)
+    ncp = max(2, int(np.ceil(600e6 / wbytes)))
+    cps = [[(pk[0].clone(), pk[1]) for pk in packs] for _ in range(ncp)]
+    for M in c["M_list"]:
+        H = torch.from_numpy(f["H"][:M]).to(dev)
+        ws = torch.empty(B.lib().bitnet_ffn_workspace_bytes(M, D, F), dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, D), dtype=torch.float32, device=dev)
+
+        def run(i):
+            g, u, dn = cps[i % ncp]
+            B.bitnet_ffn_forward(H, None, float(np.finfo(np.float32).eps), g[0], g[1], u[0], u[1],
+                                 dn[0], dn[1], D, F, out=Y, ws=ws)
+
+        for i in range(3):
+            run(i)
+        ms, med = event_time_per_launch(run, 60, torch)
+        res[f"ffn_2b_M{M}"] = {"avg_us": round(ms * 1e3, 2),
+                               "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del cps, packs
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(d, seconds, step_bytes):
+    """The CPU oracle (as it stands) running the same decode step, on this
+    host's cores, for about `seconds` of work."""
+    import oracle
+    gu, tu, _ = oracle.quantize_weights(d["W_up"])
+    gd, td, _ = oracle.quantize_weights(d["W_down"])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.bitlinear(d["x"], tu, gu)
+        oracle.bitlinear(d["x_d"], td, gd)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(step_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "ms_per_step": round(dt * 1e3 / n, 3),
+            "sample": f"{n} oracle decode steps (quant + int matmul + dequant, up and down) "
+                      f"in {dt:.1f} s; same packed-weight byte count per step as the GPU"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libbitlinear.so (declared in include/bitlinear.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch provides device memory (output tensors are allocated with
+torch on the input's device) and the current stream.  There is no fallback:
+if the library is missing, or a tensor is not on a GPU, a call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
+
+BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP = range(6)
+BL_TERNARY, BL_BINARY = 0, 1
+BL_F32, BL_BF16 = 0, 1
+BL_KERNEL_AUTO, BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_TILED = range(4)
+FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "GH", "QH", "RSH", "GHP")
+
+_lib = None
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_str(status)})")
+
+
+def lib():
+    """The loaded library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m ternary_weight_linear_ternarize_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ, I, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    L.bl_padded_k.argtypes = [I64]
+    L.bl_padded_k.restype = I64
+    L.bl_packed_bytes.argtypes = [I64, I64]
+    L.bl_packed_bytes.restype = SZ
+    L.bl_pack_workspace_bytes.argtypes = [I64, I64]
+    L.bl_pack_workspace_bytes.restype = SZ
+    L.bl_status_str.argtypes = [I]
+    L.bl_status_str.restype = ctypes.c_char_p
+    L.bitlinear_pack.argtypes = [P, I64, I64, I, P, P, P, SZ, P]
+    L.bitlinear_pack.restype = I
+    L.bitlinear_quant_act.argtypes = [P, I, I64, I64, P, P, P, P]
+    L.bitlinear_quant_act.restype = I
+    L.bitlinear_forward.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, P]
+    L.bitlinear_forward.restype = I
+    L.bitlinear_forward_kernel.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, I, P]
+    L.bitlinear_forward_kernel.restype = I
+    L.bitnet_ffn_workspace_layout.argtypes = [I64, I64, I64, P]
+    L.bitnet_ffn_workspace_layout.restype = SZ
+    L.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
+    L.bitnet_ffn_workspace_bytes.restype = SZ
+    L.bitnet_ffn_forward.argtypes = [P, I, I64, I64, I64, P, F, P, P, P, P, P, P, P, P, SZ, P]
+    L.bitnet_ffn_forward.restype = I
+    _lib = L
+    return L
+
+
+def status_str(status):
+    return lib().bl_status_str(int(status)).decode()
+
+
+def _check(status, where):
+    if status != BL_OK:
+        raise BitLinearError(status, where)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name):
+    return None if t is None else _dev(t, name)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def padded_k(K):
+    return int(lib().bl_padded_k(int(K)))
+
+
+def ffn_workspace_layout(M, D, F):
+    off = (ctypes.c_size_t * len(FFN_WS_NAMES))()
+    total = lib().bitnet_ffn_workspace_layout(int(M), int(D), int(F), off)
+    return int(total), {n: int(off[i]) for i, n in enumerate(FFN_WS_NAMES)}
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+
+def bitlinear_pack(W, mode=BL_TERNARY, out=None, scale=None, ws=None):
+    """Quantise and pack W [N, K] float32 -> (Wp uint32 [N, Kp/16] as int32, w_scale [1])."""
+    N, K = W.shape
+    kp = padded_k(K)
+    dev = W.device
+    Wp = out if out is not None else torch.empty((N, kp // 16), dtype=torch.int32, device=dev)
+    sc = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    nws = lib().bl_pack_workspace_bytes(N, K)
+    ws = ws if ws is not None else torch.empty(nws, dtype=torch.uint8, device=dev)
+    st = lib().bitlinear_pack(_dev(W, "W"), N, K, int(mode), _dev(Wp, "Wp"), _dev(sc, "w_scale"),
+                              _dev(ws, "ws"), ws.numel(), _stream(dev))
+    _check(st, "bitlinear_pack")
+    return Wp, sc
+
+
+def bitlinear_quant_act(X, out=None):
+    """X [M, K] float32/bfloat16 -> (Xq int8 [M, Kp], x_scale [M], x_rowsum int32 [M])."""
+    M, K = X.shape
+    if X.dtype == torch.float32:
+        dt = BL_F32
+    elif X.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise ValueError("X must be float32 or bfloat16")
+    dev = X.device
+    if out is None:
+        out = (torch.empty((M, padded_k(K)), dtype=torch.int8, device=dev),
+               torch.empty(M, dtype=torch.float32, device=dev),
+               torch.empty(M, dtype=torch.int32, device=dev))
+    Xq, xs, rs = out
+    st = lib().bitlinear_quant_act(_dev(X, "X"), dt, M, K, _dev(Xq, "Xq"), _dev(xs, "x_scale"),
+                                   _opt(rs, "x_rowsum"), _stream(dev))
+    _check(st, "bitlinear_quant_act")
+    return Xq, xs, rs
+
+
+def bitlinear_forward(Xq, x_scale, x_rowsum, K, Wp, w_scale, N, with_acc=False,
+                      kernel=BL_KERNEL_AUTO, out=None, acc_out=None):
+    """Y [M, N] float32 (and the int32 accumulators when with_acc)."""
+    M = Xq.shape[0]
+    dev = Xq.device
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    acc = acc_out
+    if with_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    st = lib().bitlinear_forward_kernel(
+        _dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(x_rowsum, "x_rowsum"), M, K,
+        _dev(Wp, "Wp"), _dev(w_scale, "w_scale"), N, _dev(Y, "Y"), _opt(acc, "acc_out"),
+        int(kernel), _stream(dev))
+    _check(st, "bitlinear_forward")
+    return (Y, acc) if with_acc else Y
+
+
+def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=None, ws=None):
+    """FFN block; returns (Y [M, D] float32, workspace uint8 tensor)."""
+    M = H.shape[0]
+    if H.dtype == torch.float32:
+        dt = BL_F32
+    elif H.dtype == torch.bfloat16:
+        dt = BL_BF16
+    else:
+        raise ValueError("H must be float32 or bfloat16")
+    dev = H.device
+    Y = out if out is not None else torch.empty((M, D), dtype=torch.float32, device=dev)
+    nws = lib().bitnet_ffn_workspace_bytes(M, D, F)
+    ws = ws if ws is not None else torch.empty(nws, dtype=torch.uint8, device=dev)
+    st = lib().bitnet_ffn_forward(
+        _dev(H, "H"), dt, M, D, F, _opt(norm_w, "norm_w"), float(norm_eps),
+        _dev(Wg, "Wg"), _dev(sg, "sg"), _dev(Wu, "Wu"), _dev(su, "su"),
+        _dev(Wd, "Wd"), _dev(sd, "sd"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel(), _stream(dev))
+    _check(st, "bitnet_ffn_forward")
+    return Y, ws
+
+
+def ffn_internals(ws, M, D, F):
+    """Views of the FFN workspace regions (see bitnet_ffn_workspace_layout)."""
+    _, off = ffn_workspace_layout(M, D, F)
+    dp, fp = padded_k(D), padded_k(F)
+
+    def view(name, dtype, count, shape):
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return ws[off[name]:off[name] + nbytes].view(dtype).reshape(shape)
+
+    return {
+        "xn": view("XN", torch.float32, M * D, (M, D)),
+        "qx": view("QX", torch.int8, M * dp, (M, dp)),
+        "gx": view("GX", torch.float32, M, (M,)),
+        "rsx": view("RSX", torch.int32, M, (M,)),
+        "h": view("H", torch.float32, M * F, (M, F)),
+        "gh": view("GH", torch.float32, M, (M,)),
+        "qh": view("QH", torch.int8, M * fp, (M, fp)),
+        "rsh": view("RSH", torch.int32, M, (M,)),
+    }

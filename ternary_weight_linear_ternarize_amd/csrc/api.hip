@@ -1,0 +1,188 @@
+// C ABI of the BitLinear library: host-side validation, workspace layout and
+// kernel dispatch.  Nothing here touches device memory on the host, allocates
+// or synchronises; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bitlinear.h"
+#include "bl_launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool dim_ok(int64_t v) { return v >= 1 && v <= BL_MAX_DIM; }
+bool m_ok(int64_t v) { return v >= 1 && v <= BL_MAX_M; }
+int64_t padk(int64_t K) { return (K + 63) / 64 * 64; }
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BL_OK : BL_EHIP; }
+
+int check_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                  int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y) {
+  if (!Xq || !x_scale || !x_rowsum || !Wp || !w_scale || !Y) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(K) || !dim_ok(N)) return BL_ESHAPE;
+  if (!aligned(Xq, 16) || !aligned(Wp, 16) || !aligned(Y, 4) || !aligned(x_scale, 4) ||
+      !aligned(x_rowsum, 4) || !aligned(w_scale, 4))
+    return BL_EALIGN;
+  return BL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bl_padded_k(int64_t K) { return K <= 0 ? 0 : padk(K); }
+
+size_t bl_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)N * (size_t)padk(K) / 4;
+}
+
+size_t bl_pack_workspace_bytes(int64_t N, int64_t K) {
+  (void)N;
+  (void)K;
+  return 256 * sizeof(uint64_t);
+}
+
+const char* bl_status_str(int status) {
+  switch (status) {
+    case BL_OK: return "ok";
+    case BL_EINVAL: return "invalid argument (null pointer or unknown enum value)";
+    case BL_ESHAPE: return "invalid shape (size <= 0, above the limit, or not fitting the kernel)";
+    case BL_EALIGN: return "misaligned pointer";
+    case BL_EWORKSPACE: return "workspace missing or too small";
+    case BL_EHIP: return "HIP runtime error while enqueuing kernels";
+    default: return "unknown status";
+  }
+}
+
+int bitlinear_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp, float* w_scale,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !Wp || !w_scale) return BL_EINVAL;
+  if (mode != BL_TERNARY && mode != BL_BINARY) return BL_EINVAL;
+  if (!dim_ok(N) || !dim_ok(K)) return BL_ESHAPE;
+  if (!ws || ws_bytes < bl_pack_workspace_bytes(N, K)) return BL_EWORKSPACE;
+  if (!aligned(W, 4) || !aligned(Wp, 16) || !aligned(w_scale, 4) || !aligned(ws, 16))
+    return BL_EALIGN;
+  return hip_status(bl::launch_pack(W, N, K, mode == BL_BINARY, Wp, w_scale,
+                                    reinterpret_cast<uint64_t*>(ws), as_stream(stream)));
+}
+
+int bitlinear_quant_act(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
+                        float* x_scale, int32_t* x_rowsum, void* stream) {
+  if (!X || !Xq || !x_scale) return BL_EINVAL;
+  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(K)) return BL_ESHAPE;
+  if (!aligned(X, dtype == BL_F32 ? 4 : 2) || !aligned(Xq, 16) || !aligned(x_scale, 4) ||
+      (x_rowsum && !aligned(x_rowsum, 4)))
+    return BL_EALIGN;
+  return hip_status(bl::launch_act_quant(X, dtype == BL_BF16, M, K, Xq, x_scale, x_rowsum,
+                                         nullptr, 0, as_stream(stream)));
+}
+
+int bitlinear_forward_kernel(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
+                             int64_t M, int64_t K, const uint32_t* Wp, const float* w_scale,
+                             int64_t N, float* Y, int32_t* acc_out, int kernel, void* stream) {
+  int st = check_forward(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y);
+  if (st != BL_OK) return st;
+  if (acc_out && !aligned(acc_out, 4)) return BL_EALIGN;
+  if (kernel == BL_KERNEL_AUTO) kernel = (M == 1) ? BL_KERNEL_GEMV : (M <= 64 ? BL_KERNEL_SKINNY : BL_KERNEL_TILED);
+  hipStream_t s = as_stream(stream);
+  switch (kernel) {
+    case BL_KERNEL_GEMV:
+      if (M != 1) return BL_ESHAPE;
+      return hip_status(bl::launch_gemv(Xq, x_scale, x_rowsum, K, Wp, w_scale, N, Y, acc_out, s));
+    case BL_KERNEL_SKINNY:
+      if (M > 64) return BL_ESHAPE;
+      return hip_status(
+          bl::launch_mfma(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y, acc_out, false, s));
+    case BL_KERNEL_TILED:
+      return hip_status(
+          bl::launch_mfma(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y, acc_out, true, s));
+    default:
+      return BL_EINVAL;
+  }
+}
+
+int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum, int64_t M,
+                      int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
+                      int32_t* acc_out, void* stream) {
+  return bitlinear_forward_kernel(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y, acc_out,
+                                  BL_KERNEL_AUTO, stream);
+}
+
+size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off) {
+  if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return 0;
+  const size_t m = (size_t)M;
+  int64_t parts = bl::gemv_gateup_parts(F);
+  const int64_t p2 = bl::mfma_gateup_parts(M, F);
+  if (p2 > parts) parts = p2;
+  const size_t sizes[BL_FFN_WS_COUNT] = {
+      m * (size_t)D * 4,       // XN
+      m * (size_t)padk(D),     // QX
+      m * 4,                   // GX
+      m * 4,                   // RSX
+      m * (size_t)F * 4,       // H
+      m * 4,                   // GH
+      m * (size_t)padk(F),     // QH
+      m * 4,                   // RSH
+      m * (size_t)parts * 4,   // GHP
+  };
+  size_t o = 0;
+  for (int i = 0; i < BL_FFN_WS_COUNT; ++i) {
+    if (off) off[i] = o;
+    o += up256(sizes[i]);
+  }
+  return o;
+}
+
+size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F) {
+  return bitnet_ffn_workspace_layout(M, D, F, nullptr);
+}
+
+int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
+                       const float* norm_w, float norm_eps, const uint32_t* Wg, const float* sg,
+                       const uint32_t* Wu, const float* su, const uint32_t* Wd, const float* sd,
+                       float* Y, void* ws, size_t ws_bytes, void* stream) {
+  if (!H || !Wg || !sg || !Wu || !su || !Wd || !sd || !Y) return BL_EINVAL;
+  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return BL_ESHAPE;
+  size_t off[BL_FFN_WS_COUNT];
+  const size_t need = bitnet_ffn_workspace_layout(M, D, F, off);
+  if (!ws || ws_bytes < need) return BL_EWORKSPACE;
+  if (!aligned(H, dtype == BL_F32 ? 4 : 2) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
+      !aligned(Wd, 16) || !aligned(Y, 4) || !aligned(ws, 256) || !aligned(sg, 4) ||
+      !aligned(su, 4) || !aligned(sd, 4) || (norm_w && !aligned(norm_w, 4)))
+    return BL_EALIGN;
+  char* base = reinterpret_cast<char*>(ws);
+  float* xn = reinterpret_cast<float*>(base + off[BL_FFN_WS_XN]);
+  int8_t* qx = reinterpret_cast<int8_t*>(base + off[BL_FFN_WS_QX]);
+  float* gx = reinterpret_cast<float*>(base + off[BL_FFN_WS_GX]);
+  int32_t* rsx = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_RSX]);
+  float* h = reinterpret_cast<float*>(base + off[BL_FFN_WS_H]);
+  float* gh = reinterpret_cast<float*>(base + off[BL_FFN_WS_GH]);
+  int8_t* qh = reinterpret_cast<int8_t*>(base + off[BL_FFN_WS_QH]);
+  int32_t* rsh = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_RSH]);
+  float* ghp = reinterpret_cast<float*>(base + off[BL_FFN_WS_GHP]);
+  hipStream_t s = as_stream(stream);
+  const bool bf16 = dtype == BL_BF16;
+
+  hipError_t e = bl::launch_rmsnorm_quant(H, bf16, M, D, norm_w, norm_eps, xn, qx, gx, rsx, s);
+  if (e != hipSuccess) return BL_EHIP;
+  int nparts = 0;
+  if (M == 1)
+    e = bl::launch_gemv_gateup(qx, gx, rsx, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
+  else
+    e = bl::launch_mfma_gateup(qx, gx, rsx, M, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
+  if (e != hipSuccess) return BL_EHIP;
+  e = bl::launch_act_quant(h, false, M, F, qh, gh, rsh, ghp, nparts, s);
+  if (e != hipSuccess) return BL_EHIP;
+  if (M == 1)
+    e = bl::launch_gemv(qh, gh, rsh, F, Wd, sd, D, Y, nullptr, s);
+  else
+    e = bl::launch_mfma(qh, gh, rsh, M, F, Wd, sd, D, Y, nullptr, M > 64, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

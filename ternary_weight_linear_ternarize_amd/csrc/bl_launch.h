@@ -1,0 +1,53 @@
+// Internal launchers of the gfx950 kernels (host side).  All enqueue on the
+// given stream and return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bl {
+
+// bitlinear_pack: zero bins, exponent-binned exact |w| sum, finalize g_w,
+// ternarise/binarise + pack.
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, int binary, uint32_t* Wp,
+                       float* w_scale, uint64_t* bins, hipStream_t s);
+
+// Per-token absmax int8 quantisation.  When gamma_parts is non-null the
+// scale of row m is max over p < nparts of gamma_parts[p * M + m] (partial
+// maxima written by another kernel) instead of being computed from X.
+hipError_t launch_act_quant(const void* X, bool bf16, int64_t M, int64_t K, int8_t* Xq,
+                            float* x_scale, int32_t* rowsum, const float* gamma_parts,
+                            int nparts, hipStream_t s);
+
+// RMSNorm + per-token quantisation of the normalised rows.
+hipError_t launch_rmsnorm_quant(const void* H, bool bf16, int64_t M, int64_t D,
+                                const float* norm_w, float eps, float* xn, int8_t* Xq,
+                                float* x_scale, int32_t* rowsum, hipStream_t s);
+
+// Y = dequant(Xq . T^T) for one token (M == 1): the dot4 GEMV.
+hipError_t launch_gemv(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t K,
+                       const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
+                       int32_t* acc_out, hipStream_t s);
+
+// Y = dequant(Xq . T^T) on MFMA: skinny (M <= 64, tiled == false) or the
+// 128 x 128 tiled kernel.
+hipError_t launch_mfma(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,
+                       int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
+                       int32_t* acc_out, bool tiled, hipStream_t s);
+
+// FFN gate/up: h = relu(deq(gate))^2 * deq(up) for both weights at once, plus
+// per-block partial maxima of |h| (gh_parts[p * M + m], p < *nparts).
+hipError_t launch_gemv_gateup(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
+                              int64_t K, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
+                              const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
+                              hipStream_t s);
+hipError_t launch_mfma_gateup(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
+                              int64_t M, int64_t K, const uint32_t* Wg, const float* sg,
+                              const uint32_t* Wu, const float* su, int64_t N, float* H,
+                              float* gh_parts, int* nparts, hipStream_t s);
+
+// Upper bounds of the partial-maximum slots per row the gate/up kernels write.
+int64_t gemv_gateup_parts(int64_t N);
+int64_t mfma_gateup_parts(int64_t M, int64_t N);
+
+}  // namespace bl

@@ -1,0 +1,301 @@
+// Ternary x int8 matrix product on the gfx950 matrix cores (MFMA), for more
+// than one token: Y[m][n] = dequant(sum_k q[m][k] * t[n][k]).
+//
+// youngju.dev "BitNet論文分析", section "BitNet b1.58": the integer product is
+// F.linear(x_q, w_q) followed by output * (w_scale * x_scale) / Q.
+// dashen-tech "BitNet.cpp 深度解析" §3.1: it equals sum_pos - sum_neg.  With
+// many tokens it is a dense contraction, so it runs on
+// v_mfma_i32_16x16x64_i8 in the shifted-code form
+//   acc = sum_k q[m][k] * (t[n][k] + 1) - rowsum[m],
+// where a 2-bit word unpacks into an MFMA operand with four shift+mask ops:
+// word j of a row holds weight 16j + 4s + b in byte b at bits 2s, so
+// (w >> 2s) & 0x03030303 are the codes of weights 16j+4s..16j+4s+3 in order.
+//
+// Tiling: a 256-thread block (4 waves, WAVES_M x WAVES_N) computes a
+// BM x BN tile of Y, BM = 16*TM*WAVES_M, BN = 16*TN*WAVES_N; each wave owns
+// TM x TN 16x16 accumulator tiles.  K advances in chunks of 256: the
+// activation chunk (BM x 256 int8) is staged through LDS (double buffered,
+// one barrier per chunk); the packed weight chunk (16 bytes per lane per
+// 16-row tile) goes straight from memory to registers and is unpacked there.
+// Both are prefetched one chunk ahead.
+//
+// MFMA operand mapping (lane l, g = l / 16): A lane l supplies token row
+// l % 16 and B lane l weight row l % 16, each with 16 k-values; result lane
+// l, register r holds (token 4g + r, weight row l % 16).  In k-step s of a
+// chunk, lane group g uses packed word 4g + s of the chunk (weights
+// 16(4g+s) .. +15) and the matching 16 activation bytes at offset 64g + 16s.
+#include "bl_device.h"
+#include "bl_launch.h"
+
+namespace bl {
+
+enum { MF_STORE = 0, MF_GATEUP = 1 };
+
+constexpr int kChunk = 256;         // K per chunk
+constexpr int kLdsPitch = 256 + 16; // bytes per staged activation row
+
+__device__ __forceinline__ v4i unpack_operand(uint32_t w) {
+  v4i r;
+  r[0] = (int)(w & 0x03030303u);
+  r[1] = (int)((w >> 2) & 0x03030303u);
+  r[2] = (int)((w >> 4) & 0x03030303u);
+  r[3] = (int)((w >> 6) & 0x03030303u);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
+  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
+template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
+__global__ __launch_bounds__(256) void mfma_gemm_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp,
+    const uint32_t* __restrict__ W0, const float* __restrict__ s0,
+    const uint32_t* __restrict__ W1, const float* __restrict__ s1, int64_t N,
+    float* __restrict__ Y, int32_t* __restrict__ acc_out, float* __restrict__ gh_parts,
+    int nbn) {
+  static_assert(WAVES_M * WAVES_N == 4, "4 waves per block");
+  constexpr int BM = 16 * TM * WAVES_M;
+  constexpr int BN = 16 * TN * WAVES_N;
+  constexpr int NB = (EPI == MF_GATEUP) ? 2 : 1;       // weight matrices
+  constexpr int A_U4 = BM * (kChunk / 16) / 256;       // uint4 per thread per chunk
+  constexpr int A_U4_PAD = A_U4 > 0 ? A_U4 : 1;
+  __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * kLdsPitch];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int g = lane >> 4, li = lane & 15;
+  const int bn = blockIdx.x % nbn, bm = blockIdx.x / nbn;
+  const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
+  const int64_t wpr = Kp / 16;
+  const int64_t nchunks = (Kp + kChunk - 1) / kChunk;
+
+  // ---- loaders
+  uint4 a_reg[A_U4_PAD];
+  auto load_a = [&](int64_t kc) {
+    if constexpr (A_U4 > 0) {
+#pragma unroll
+      for (int i = 0; i < A_U4; ++i) {
+        const int u = tid + 256 * i;
+        const int row = u >> 4, c16 = u & 15;
+        const int64_t m = m0 + row, k = kc + 16 * c16;
+        if (m < M && k < Kp)
+          a_reg[i] = *reinterpret_cast<const uint4*>(Xq + m * Kp + k);
+        else
+          a_reg[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      // fewer than 256 uint4 per chunk: threads beyond BM*16 idle
+      const int u = tid;
+      const int row = u >> 4, c16 = u & 15;
+      const int64_t m = m0 + row, k = kc + 16 * c16;
+      if (row < BM && m < M && k < Kp)
+        a_reg[0] = *reinterpret_cast<const uint4*>(Xq + m * Kp + k);
+      else
+        a_reg[0] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_a = [&](int buf) {
+    if constexpr (A_U4 > 0) {
+#pragma unroll
+      for (int i = 0; i < A_U4; ++i) {
+        const int u = tid + 256 * i;
+        const int row = u >> 4, c16 = u & 15;
+        *reinterpret_cast<uint4*>(&lds_a[buf][row * kLdsPitch + 16 * c16]) = a_reg[i];
+      }
+    } else {
+      const int u = tid;
+      const int row = u >> 4, c16 = u & 15;
+      if (row < BM) *reinterpret_cast<uint4*>(&lds_a[buf][row * kLdsPitch + 16 * c16]) = a_reg[0];
+    }
+  };
+  uint4 b_reg[NB][TN];
+  auto load_b = [&](int64_t kc) {
+#pragma unroll
+    for (int mat = 0; mat < NB; ++mat) {
+      const uint32_t* W = (mat == 0) ? W0 : W1;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int64_t n = n0 + 16 * (wn * TN + tn) + li;
+        const int64_t word = kc / 16 + 4 * g;
+        if (n < N && word < wpr)
+          b_reg[mat][tn] = *reinterpret_cast<const uint4*>(W + n * wpr + word);
+        else
+          b_reg[mat][tn] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
+  v4i acc[NB][TM][TN];
+#pragma unroll
+  for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[mat][tm][tn] = v4i{0, 0, 0, 0};
+
+  load_a(0);
+  load_b(0);
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int buf = (int)(c & 1);
+    store_a(buf);
+    uint4 b_cur[NB][TN];
+#pragma unroll
+    for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) b_cur[mat][tn] = b_reg[mat][tn];
+    __syncthreads();
+    if (c + 1 < nchunks) {
+      load_a((c + 1) * kChunk);
+      load_b((c + 1) * kChunk);
+    }
+    const int8_t* la = &lds_a[buf][0];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i a[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int row = 16 * (wm * TM + tm) + li;
+        a[tm] = *reinterpret_cast<const v4i*>(la + row * kLdsPitch + 64 * g + 16 * s);
+      }
+#pragma unroll
+      for (int mat = 0; mat < NB; ++mat) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const v4i b = unpack_operand(pick(b_cur[mat][tn], s));
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+            acc[mat][tm][tn] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(a[tm], b, acc[mat][tm][tn], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue
+  if constexpr (EPI == MF_STORE) {
+    const float sw = s0[0];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + 16 * (wm * TM + tm) + 4 * g + r;
+        if (m >= M) continue;
+        const int32_t rsm = rowsum[m];
+        const float sc = __fmul_rn(sw, x_scale[m]);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int64_t n = n0 + 16 * (wn * TN + tn) + li;
+          if (n < N) {
+            const int a = acc[0][tm][tn][r] - rsm;
+            Y[m * N + n] = dequant(a, sc);
+            if (acc_out) acc_out[m * N + n] = a;
+          }
+        }
+      }
+    }
+  } else {
+    __shared__ float red[WAVES_N][BM];
+    const float sg = s0[0], su = s1[0];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = 16 * (wm * TM + tm) + 4 * g + r;
+        const int64_t m = m0 + lrow;
+        float hmax = 0.0f;
+        if (m < M) {
+          const int32_t rsm = rowsum[m];
+          const float xs = x_scale[m];
+          const float scg = __fmul_rn(sg, xs), scu = __fmul_rn(su, xs);
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const int64_t n = n0 + 16 * (wn * TN + tn) + li;
+            if (n < N) {
+              const float gv = dequant(acc[0][tm][tn][r] - rsm, scg);
+              const float uv = dequant(acc[1][tm][tn][r] - rsm, scu);
+              const float a = gv > 0.0f ? gv : 0.0f;
+              const float h = __fmul_rn(__fmul_rn(a, a), uv);
+              Y[m * N + n] = h;
+              hmax = fmaxf(hmax, fabsf(h));
+            }
+          }
+        }
+        // max over the 16 lanes holding this row
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+        if (li == 0) red[wn][lrow] = hmax;
+      }
+    }
+    __syncthreads();
+    for (int lrow = tid; lrow < BM; lrow += 256) {
+      float v = red[0][lrow];
+#pragma unroll
+      for (int w = 1; w < WAVES_N; ++w) v = fmaxf(v, red[w][lrow]);
+      const int64_t m = m0 + lrow;
+      if (m < M) gh_parts[(int64_t)bn * M + m] = v;
+    }
+  }
+}
+
+template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
+static hipError_t mfma_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                              int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
+                              const float* s1, int64_t N, float* Y, int32_t* acc_out,
+                              float* gh_parts, int* nparts, hipStream_t s) {
+  constexpr int BM = 16 * TM * WAVES_M;
+  constexpr int BN = 16 * TN * WAVES_N;
+  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  if (nparts) *nparts = (int)nbn;
+  hipLaunchKernelGGL((mfma_gemm_kernel<TM, TN, WAVES_M, WAVES_N, EPI>), dim3((unsigned)(nbm * nbn)),
+                     dim3(256), 0, s, Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts,
+                     (int)nbn);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M, int64_t K,
+                       const uint32_t* Wp, const float* ws, int64_t N, float* Y, int32_t* acc_out,
+                       bool tiled, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  if (tiled || M > 64)
+    return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                             acc_out, nullptr, nullptr, s);
+  if (M <= 16)
+    return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                             acc_out, nullptr, nullptr, s);
+  if (M <= 32)
+    return mfma_launch<2, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                             acc_out, nullptr, nullptr, s);
+  if (M <= 64)
+    return mfma_launch<4, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                             acc_out, nullptr, nullptr, s);
+  return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                           acc_out, nullptr, nullptr, s);
+}
+
+int64_t mfma_gateup_parts(int64_t M, int64_t N) {
+  // the narrowest block used by launch_mfma_gateup is 64 columns
+  (void)M;
+  return (N + 63) / 64;
+}
+
+hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                              int64_t K, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
+                              const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
+                              hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  if (M <= 16)
+    return mfma_launch<1, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                              gh_parts, nparts, s);
+  if (M <= 32)
+    return mfma_launch<2, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                              gh_parts, nparts, s);
+  if (M <= 64)
+    return mfma_launch<4, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                              gh_parts, nparts, s);
+  return mfma_launch<4, 4, 2, 2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                            gh_parts, nparts, s);
+}
+
+}  // namespace bl

@@ -1,0 +1,166 @@
+// Activation quantisation kernels on gfx950.
+//
+// youngju.dev "BitNet論文分析", section "BitNet b1.58" (activation_quant of
+// BitLinear_b158): per token, scale = max |x| over the row, codes =
+// clamp(round(x * Q / (scale + 1e-5))); Q = 127 and the symmetric range
+// [-127, 127] (ai-heartland "BitLinearの仕組み": codes in {-Qb..Qb}).
+// The same listing normalises with nn.RMSNorm before quantising; the
+// RMSNorm kernel below makes the mean square exact and order-free (integer
+// exponent bins of m^2, rounded once to binary64).
+//
+// One 256-thread block per token row.  Codes are written four per 32-bit
+// store into rows of Kp bytes; the padding columns get code 0.
+#include "bl_device.h"
+#include "bl_launch.h"
+
+namespace bl {
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return v;
+}
+
+// Writes the int8 codes of row values f(k) (k < K; 0 beyond) into q[0..Kp)
+// and returns this thread's share of their sum.
+template <typename F>
+__device__ __forceinline__ int write_codes(F f, int64_t K, int64_t Kp, float d, int8_t* q) {
+  int rs = 0;
+  uint32_t* q32 = reinterpret_cast<uint32_t*>(q);
+  for (int64_t w = threadIdx.x; w < Kp / 4; w += blockDim.x) {
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t k = 4 * w + b;
+      int c = 0;
+      if (k < K) c = quant_code(f(k), d);
+      rs += c;
+      packed |= ((uint32_t)(c & 0xff)) << (8 * b);
+    }
+    q32[w] = packed;
+  }
+  return rs;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ X, int64_t K,
+                                                        int64_t Kp, int8_t* __restrict__ Xq,
+                                                        float* __restrict__ x_scale,
+                                                        int32_t* __restrict__ rowsum,
+                                                        const float* __restrict__ gamma_parts,
+                                                        int nparts, int64_t M) {
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int64_t m = blockIdx.x;
+  const char* base = reinterpret_cast<const char*>(X) + m * K * (BF16 ? 2 : 4);
+  float g = 0.0f;
+  if (gamma_parts) {
+    for (int p = threadIdx.x; p < nparts; p += blockDim.x) g = fmaxf(g, gamma_parts[(int64_t)p * M + m]);
+  } else {
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) g = fmaxf(g, fabsf(load_act<BF16>(base, k)));
+  }
+  g = block_max(g, redf);
+  const float d = __fadd_rn(g, kEps);
+  int rs = write_codes([&](int64_t k) { return load_act<BF16>(base, k); }, K, Kp, d, Xq + m * Kp);
+  rs = block_sum(rs, redi);
+  if (threadIdx.x == 0) {
+    x_scale[m] = g;
+    if (rowsum) rowsum[m] = rs;
+  }
+}
+
+// RMSNorm(D) of one row, then its int8 codes.  xn = (x * r) * w with
+// r = 1 / sqrt(ms + eps), ms = binary32(binary64(exact sum x^2) / D).
+template <bool BF16>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
+    const void* __restrict__ H, int64_t D, int64_t Dp, const float* __restrict__ norm_w,
+    float eps, float* __restrict__ xn, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
+    int32_t* __restrict__ rowsum) {
+  __shared__ unsigned long long bins[4][kBins];
+  __shared__ uint64_t tot[kBins];
+  __shared__ unsigned long long limbs[kLimbs];
+  __shared__ double res;
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t m = blockIdx.x;
+  const char* base = reinterpret_cast<const char*>(H) + m * D * (BF16 ? 2 : 4);
+  for (int i = tid; i < 4 * kBins; i += 256) (&bins[0][0])[i] = 0ull;
+  __syncthreads();
+  for (int64_t k = tid; k < D; k += 256) {
+    int b;
+    uint32_t mm;
+    bin_of(load_act<BF16>(base, k), b, mm);
+    if (mm) atomicAdd(&bins[wave][b], (unsigned long long)mm * (unsigned long long)mm);
+  }
+  __syncthreads();
+  for (int b = tid; b < kBins; b += 256) tot[b] = bins[0][b] + bins[1][b] + bins[2][b] + bins[3][b];
+  __syncthreads();
+  const double s = finalize_bins<2>(tot, limbs, &res);
+  const float ms = (float)(s / (double)D);
+  // __builtin_sqrtf is correctly rounded under -fhip-fp32-correctly-rounded-divide-sqrt
+  // (the __fsqrt_rn intrinsic maps to a native approximation on this toolchain).
+  const float r = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(ms, eps)));
+  auto norm = [&](int64_t k) {
+    float v = __fmul_rn(load_act<BF16>(base, k), r);
+    return norm_w ? __fmul_rn(v, norm_w[k]) : v;
+  };
+  float g = 0.0f;
+  for (int64_t k = tid; k < D; k += 256) {
+    const float v = norm(k);
+    xn[m * D + k] = v;
+    g = fmaxf(g, fabsf(v));
+  }
+  g = block_max(g, redf);
+  const float d = __fadd_rn(g, kEps);
+  int rs = write_codes(norm, D, Dp, d, Xq + m * Dp);
+  rs = block_sum(rs, redi);
+  if (tid == 0) {
+    x_scale[m] = g;
+    rowsum[m] = rs;
+  }
+}
+
+hipError_t launch_act_quant(const void* X, bool bf16, int64_t M, int64_t K, int8_t* Xq,
+                            float* x_scale, int32_t* rowsum, const float* gamma_parts,
+                            int nparts, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  if (bf16)
+    hipLaunchKernelGGL(act_quant_kernel<true>, dim3((unsigned)M), dim3(256), 0, s, X, K, Kp, Xq,
+                       x_scale, rowsum, gamma_parts, nparts, M);
+  else
+    hipLaunchKernelGGL(act_quant_kernel<false>, dim3((unsigned)M), dim3(256), 0, s, X, K, Kp, Xq,
+                       x_scale, rowsum, gamma_parts, nparts, M);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quant(const void* H, bool bf16, int64_t M, int64_t D,
+                                const float* norm_w, float eps, float* xn, int8_t* Xq,
+                                float* x_scale, int32_t* rowsum, hipStream_t s) {
+  const int64_t Dp = (D + 63) / 64 * 64;
+  if (bf16)
+    hipLaunchKernelGGL(rmsnorm_quant_kernel<true>, dim3((unsigned)M), dim3(256), 0, s, H, D, Dp,
+                       norm_w, eps, xn, Xq, x_scale, rowsum);
+  else
+    hipLaunchKernelGGL(rmsnorm_quant_kernel<false>, dim3((unsigned)M), dim3(256), 0, s, H, D, Dp,
+                       norm_w, eps, xn, Xq, x_scale, rowsum);
+  return hipGetLastError();
+}
+
+}  // namespace bl

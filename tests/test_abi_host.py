@@ -1,0 +1,127 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every function include/bitlinear.h declares, and rejects bad arguments on the
+host before anything is enqueued.  Pointers passed here are fake non-null
+addresses: validation never dereferences them, and every call below fails
+validation, so no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_weight_linear_ternarize_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # 64 KiB: aligned to anything we check
+ODD = ctypes.c_void_p(0x10001)       # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    names = declared_functions()
+    assert "bitlinear_pack" in names and "bitnet_ffn_forward" in names
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_size_helpers():
+    lib = B.lib()
+    assert lib.bl_padded_k(1) == 64 and lib.bl_padded_k(64) == 64 and lib.bl_padded_k(65) == 128
+    assert lib.bl_padded_k(0) == 0
+    assert lib.bl_packed_bytes(6912, 2560) == 4423680
+    assert lib.bl_packed_bytes(28672, 8192) == 58720256
+    assert lib.bl_packed_bytes(400, 512) == 51200
+    assert lib.bl_pack_workspace_bytes(10, 10) >= 256 * 8
+    total, off = B.ffn_workspace_layout(8, 2560, 6912)
+    assert all(v % 256 == 0 for v in off.values())
+    assert off["QX"] - off["XN"] >= 8 * 2560 * 4
+    assert off["QH"] + 8 * 6912 <= total
+    assert lib.bitnet_ffn_workspace_bytes(8, 2560, 6912) == total
+
+
+def test_status_strings():
+    for s in range(6):
+        assert B.status_str(s)
+    assert B.status_str(99) == "unknown status"
+
+
+def test_pack_validation():
+    lib = B.lib()
+    ws_n = lib.bl_pack_workspace_bytes(4, 4)
+    assert lib.bitlinear_pack(None, 4, 4, 0, FAKE, FAKE, FAKE, ws_n, None) == B.BL_EINVAL
+    assert lib.bitlinear_pack(FAKE, 4, 4, 7, FAKE, FAKE, FAKE, ws_n, None) == B.BL_EINVAL
+    assert lib.bitlinear_pack(FAKE, 0, 4, 0, FAKE, FAKE, FAKE, ws_n, None) == B.BL_ESHAPE
+    assert lib.bitlinear_pack(FAKE, 4, 70000, 0, FAKE, FAKE, FAKE, ws_n, None) == B.BL_ESHAPE
+    assert lib.bitlinear_pack(FAKE, 4, 4, 0, FAKE, FAKE, FAKE, ws_n - 1, None) == B.BL_EWORKSPACE
+    assert lib.bitlinear_pack(FAKE, 4, 4, 0, FAKE, FAKE, None, ws_n, None) == B.BL_EWORKSPACE
+    assert lib.bitlinear_pack(FAKE, 4, 4, 0, ODD, FAKE, FAKE, ws_n, None) == B.BL_EALIGN
+
+
+def test_quant_validation():
+    lib = B.lib()
+    assert lib.bitlinear_quant_act(None, 0, 1, 8, FAKE, FAKE, FAKE, None) == B.BL_EINVAL
+    assert lib.bitlinear_quant_act(FAKE, 2, 1, 8, FAKE, FAKE, FAKE, None) == B.BL_EINVAL
+    assert lib.bitlinear_quant_act(FAKE, 0, 0, 8, FAKE, FAKE, FAKE, None) == B.BL_ESHAPE
+    assert lib.bitlinear_quant_act(FAKE, 0, 1, -1, FAKE, FAKE, FAKE, None) == B.BL_ESHAPE
+    assert lib.bitlinear_quant_act(FAKE, 0, 1, 8, ODD, FAKE, FAKE, None) == B.BL_EALIGN
+    assert lib.bitlinear_quant_act(ODD, 0, 1, 8, FAKE, FAKE, FAKE, None) == B.BL_EALIGN
+
+
+def test_forward_validation():
+    lib = B.lib()
+    f = lib.bitlinear_forward_kernel
+    args = [FAKE, FAKE, FAKE, 1, 64, FAKE, FAKE, 16, FAKE, None]
+    assert f(None, *args[1:], 0, None) == B.BL_EINVAL
+    a = list(args); a[2] = None  # rowsum is required
+    assert f(*a, 0, None) == B.BL_EINVAL
+    a = list(args); a[3] = 0
+    assert f(*a, 0, None) == B.BL_ESHAPE
+    a = list(args); a[7] = 0
+    assert f(*a, 0, None) == B.BL_ESHAPE
+    a = list(args); a[5] = ODD
+    assert f(*a, 0, None) == B.BL_EALIGN
+    a = list(args); a[3] = 2
+    assert f(*a, B.BL_KERNEL_GEMV, None) == B.BL_ESHAPE   # GEMV needs M == 1
+    a = list(args); a[3] = 65
+    assert f(*a, B.BL_KERNEL_SKINNY, None) == B.BL_ESHAPE  # skinny needs M <= 64
+    assert f(*args, 9, None) == B.BL_EINVAL
+    assert lib.bitlinear_forward(FAKE, FAKE, FAKE, 1, 64, ODD, FAKE, 16, FAKE, None, None) == B.BL_EALIGN
+
+
+def test_ffn_validation():
+    lib = B.lib()
+    M, D, F = 2, 64, 128
+    n = lib.bitnet_ffn_workspace_bytes(M, D, F)
+    base = [FAKE, 0, M, D, F, None, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, None]
+    a = list(base); a[0] = None
+    assert lib.bitnet_ffn_forward(*a) == B.BL_EINVAL
+    a = list(base); a[1] = 5
+    assert lib.bitnet_ffn_forward(*a) == B.BL_EINVAL
+    a = list(base); a[4] = 0
+    assert lib.bitnet_ffn_forward(*a) == B.BL_ESHAPE
+    a = list(base); a[15] = n - 1
+    assert lib.bitnet_ffn_forward(*a) == B.BL_EWORKSPACE
+    a = list(base); a[14] = ctypes.c_void_p(0x10010)  # 16 B aligned, not 256
+    assert lib.bitnet_ffn_forward(*a) == B.BL_EALIGN
+    a = list(base); a[7] = ODD
+    assert lib.bitnet_ffn_forward(*a) == B.BL_EALIGN
+
+
+def test_product_does_not_reference_the_oracle():
+    pkg = os.path.join(ROOT, "ternary_weight_linear_ternarize_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "liboracle" not in text and "orc_" not in text, fn

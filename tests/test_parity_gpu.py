@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, on the
+same seeded synthetic inputs.
+
+Bar: bit-exact packed words, weight scales, int8 codes, activation scales,
+row sums, int32 accumulators and FFN internals; float outputs within a
+maximum relative error of 1e-5 (in practice they are bit-identical, since the
+float steps follow the same binary32 operation order).  Every case is also
+run twice on the GPU and must repeat bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_weight_linear_ternarize_amd import binding as B
+from ternary_weight_linear_ternarize_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-5
+DEV = "cuda:0"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    _need_gpu()
+    B.lib()
+    yield
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_rel(y, ref, rtol=RTOL):
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert y.shape == ref.shape
+    err = np.abs(y - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert float(err.max(initial=0.0)) <= rtol, f"max rel err {err.max()}"
+
+
+def gpu_pack(W, mode=B.BL_TERNARY):
+    Wd = to_dev(W)
+    Wp, sc = B.bitlinear_pack(Wd, mode)
+    return Wp, sc
+
+
+def check_pack(W, mode="ternary"):
+    g, t, p = oracle.quantize_weights(W, mode)
+    Wp, sc = gpu_pack(W, B.BL_TERNARY if mode == "ternary" else B.BL_BINARY)
+    np.testing.assert_array_equal(host(Wp).view(np.uint32), p)
+    assert host(sc)[0].view(np.uint32) == np.float32(g).view(np.uint32)
+    return g, t, Wp, sc
+
+
+def check_quant(X, bf16=False):
+    xd = to_dev(X)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        X = xd.float().cpu().numpy()  # exact widening: same values for the oracle
+    q, g, rs = oracle.act_quant(X)
+    Xq, xs, xr = B.bitlinear_quant_act(xd)
+    K = X.shape[1]
+    hq = host(Xq)
+    np.testing.assert_array_equal(hq[:, :K], q)
+    assert not hq[:, K:].any()
+    np.testing.assert_array_equal(host(xs).view(np.uint32), g.view(np.uint32))
+    np.testing.assert_array_equal(host(xr), rs)
+    return q, g, rs, Xq, xs, xr
+
+
+def check_forward(q, gx, t, gw, Xq, xs, xr, Wp, ws, kernels):
+    M, K = q.shape
+    N = t.shape[0]
+    acc = oracle.int_linear(q, t)
+    y = oracle.dequant(acc, gx, gw)
+    for kern in kernels:
+        Y, A = B.bitlinear_forward(Xq, xs, xr, K, Wp, ws, N, with_acc=True, kernel=kern)
+        np.testing.assert_array_equal(host(A), acc, err_msg=f"kernel {kern}")
+        assert_rel(host(Y), y)
+        Y2 = B.bitlinear_forward(Xq, xs, xr, K, Wp, ws, N, kernel=kern)
+        np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+    return acc, y
+
+
+def kernels_for(M):
+    ks = [B.BL_KERNEL_AUTO, B.BL_KERNEL_TILED]
+    if M == 1:
+        ks.append(B.BL_KERNEL_GEMV)
+    if M <= 64:
+        ks.append(B.BL_KERNEL_SKINNY)
+    return ks
+
+
+# ----------------------------------------------------------------------------
+
+def test_single_layer_512_to_400_all_kernels():
+    d = synth.single_layer()
+    g, t, Wp, sc = check_pack(d["W"])
+    q, gx, rs, Xq, xs, xr = check_quant(d["X"])
+    check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(16))
+    # every single token through the GEMV and the MFMA kernels
+    for m in (0, 7, 15):
+        check_forward(q[m:m + 1], gx[m:m + 1], t, g, Xq[m:m + 1].contiguous(),
+                      xs[m:m + 1].contiguous(), xr[m:m + 1].contiguous(), Wp, sc, kernels_for(1))
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 1, 1), (1, 15, 17), (1, 63, 257), (1, 65, 400), (1, 1040, 33), (1, 4160, 70), (1, 16448, 9),
+    (2, 64, 16), (3, 16, 63), (5, 65, 64), (8, 1040, 257), (16, 512, 400), (17, 63, 15),
+    (31, 1000, 100), (33, 129, 65), (64, 2560, 96), (65, 300, 130), (100, 1040, 257), (129, 64, 129),
+])
+def test_random_ragged_shapes(M, K, N):
+    d = synth.random_case(1000 + M * 7 + N, M, K, N)
+    g, t, Wp, sc = check_pack(d["W"])
+    q, gx, rs, Xq, xs, xr = check_quant(d["X"])
+    check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(M))
+
+
+def test_binary_mode_and_degenerate_weights():
+    rng = np.random.default_rng(21)
+    W = rng.standard_normal((70, 200)).astype(np.float32)
+    W[3, :] = 0.0
+    W[5, 7] = -0.0
+    for mode in ("binary", "ternary"):
+        g, t, Wp, sc = check_pack(W, mode)
+        X = synth.normal(21, 1, (4, 200))
+        q, gx, rs, Xq, xs, xr = check_quant(X)
+        check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(4))
+    # all-zero and identity weights
+    check_pack(np.zeros((33, 100), np.float32))
+    g, t, Wp, sc = check_pack(np.eye(128, dtype=np.float32))
+    assert g == np.float32(1.0 / 128)
+
+
+def test_quant_edge_rows_and_bf16():
+    X = synth.normal(22, 1, (6, 700))
+    X[1] = 0.0
+    X[2] = 0.0
+    X[2, 123] = -5.0
+    X[3] = 1e-30
+    X[4] *= np.float32(1e4)
+    check_quant(X)
+    check_quant(synth.normal(23, 1, (9, 2560)), bf16=True)
+    x = synth.decode_100b(with_weights=False)["X"]
+    check_quant(x)
+
+
+def test_decode_2b_gemv_up_and_down_full():
+    d = synth.decode_2b()
+    for Wn, xn in (("W_up", "x"), ("W_down", "x_d")):
+        g, t, Wp, sc = check_pack(d[Wn])
+        zero_frac = float(np.mean(t == 0))
+        assert abs(zero_frac - 0.31) < 0.01
+        q, gx, rs, Xq, xs, xr = check_quant(d[xn])
+        check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(1))
+
+
+def test_prefill_2b_sampled_rows():
+    d = synth.prefill_2b()
+    g, t, Wp, sc = check_pack(d["W"])
+    X = d["X"]
+    q, gx, rs, Xq, xs, xr = check_quant(X)
+    M, K = X.shape
+    N = t.shape[0]
+    Y, A = B.bitlinear_forward(Xq, xs, xr, K, Wp, sc, N, with_acc=True)
+    hY, hA = host(Y), host(A)
+    rows = np.unique(np.concatenate([np.arange(0, M, 31), [M - 1]]))
+    acc = oracle.int_linear(q[rows], t)
+    np.testing.assert_array_equal(hA[rows], acc)
+    assert_rel(hY[rows], oracle.dequant(acc, gx[rows], g))
+    # properties that hold for every row: c-form identity on a column sample
+    cols = np.arange(0, N, 97)
+    tc = t[cols].astype(np.int64)
+    np.testing.assert_array_equal(hA[:, cols], q.astype(np.int64) @ tc.T)
+    Y2 = B.bitlinear_forward(Xq, xs, xr, K, Wp, sc, N)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), hY.view(np.uint32))
+
+
+@pytest.mark.parametrize("mode", ["ternary", "binary"])
+def test_decode_100b_full(mode):
+    d = synth.decode_100b()
+    g, t, Wp, sc = check_pack(d["W"], mode)
+    del d["W"]
+    for M in (1, 8):
+        q, gx, rs, Xq, xs, xr = check_quant(d["X"][:M])
+        check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(M)[:3])
+
+
+def _ffn_case(M, bf16, norm):
+    d = synth.ffn_2b(norm=norm)
+    D, F = synth.FFN_2B["D"], synth.FFN_2B["F"]
+    pk = {}
+    for name in ("W_gate", "W_up", "W_down"):
+        pk[name] = check_pack(d[name])
+    H = d["H"][:M]
+    Hd = to_dev(H)
+    if bf16:
+        Hd = Hd.to(torch.bfloat16)
+        H = Hd.float().cpu().numpy()
+    nw = d["norm_w"]
+    eps = float(np.finfo(np.float32).eps)
+    ref = oracle.ffn(H, nw, eps, pk["W_gate"][1], pk["W_gate"][0], pk["W_up"][1], pk["W_up"][0],
+                     pk["W_down"][1], pk["W_down"][0])
+    Y, ws = B.bitnet_ffn_forward(Hd, to_dev(nw), eps, pk["W_gate"][2], pk["W_gate"][3],
+                                 pk["W_up"][2], pk["W_up"][3], pk["W_down"][2], pk["W_down"][3], D, F)
+    it = {k: host(v) for k, v in B.ffn_internals(ws, M, D, F).items()}
+    np.testing.assert_array_equal(it["xn"].view(np.uint32), ref["xn"].view(np.uint32))
+    np.testing.assert_array_equal(it["qx"][:, :D], ref["qx"])
+    np.testing.assert_array_equal(it["gx"].view(np.uint32), ref["gx"].view(np.uint32))
+    np.testing.assert_array_equal(it["rsx"], ref["qx"].astype(np.int64).sum(1))
+    np.testing.assert_array_equal(it["h"].view(np.uint32), ref["h"].view(np.uint32))
+    np.testing.assert_array_equal(it["gh"].view(np.uint32), ref["gh"].view(np.uint32))
+    np.testing.assert_array_equal(it["qh"][:, :F], ref["qh"])
+    np.testing.assert_array_equal(it["rsh"], ref["qh"].astype(np.int64).sum(1))
+    assert_rel(host(Y), ref["y"])
+    Y2, _ = B.bitnet_ffn_forward(Hd, to_dev(nw), eps, pk["W_gate"][2], pk["W_gate"][3],
+                                 pk["W_up"][2], pk["W_up"][3], pk["W_down"][2], pk["W_down"][3], D, F)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_ffn_2b_fp32(M):
+    _ffn_case(M, False, "ones")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_ffn_2b_bf16_random_norm(M):
+    _ffn_case(M, True, "random")
+
+
+@pytest.mark.parametrize("M,D,F", [(1, 300, 700), (2, 64, 128), (17, 512, 1000), (100, 256, 520),
+                                   (256, 512, 1024)])
+def test_ffn_ragged_shapes(M, D, F):
+    s = 500 + M
+    x = synth.normal(s, 1, (M, D))
+    ws = [synth.normal(s, 2 + i, shp, 0.02) for i, shp in enumerate(((F, D), (F, D), (D, F)))]
+    q = [oracle.quantize_weights(w) for w in ws]
+    nw = (np.float32(1) + synth.normal(s, 9, (D,), 0.1)).astype(np.float32)
+    eps = 1e-6
+    ref = oracle.ffn(x, nw, eps, q[0][1], q[0][0], q[1][1], q[1][0], q[2][1], q[2][0])
+    pk = [B.bitlinear_pack(to_dev(w)) for w in ws]
+    for i in range(3):
+        np.testing.assert_array_equal(host(pk[i][0]).view(np.uint32), q[i][2])
+    Y, wsp = B.bitnet_ffn_forward(to_dev(x), to_dev(nw), eps, pk[0][0], pk[0][1], pk[1][0],
+                                  pk[1][1], pk[2][0], pk[2][1], D, F)
+    it = {k: host(v) for k, v in B.ffn_internals(wsp, M, D, F).items()}
+    np.testing.assert_array_equal(it["xn"].view(np.uint32), ref["xn"].view(np.uint32))
+    np.testing.assert_array_equal(it["qx"][:, :D], ref["qx"])
+    np.testing.assert_array_equal(it["h"].view(np.uint32), ref["h"].view(np.uint32))
+    np.testing.assert_array_equal(it["gh"].view(np.uint32), ref["gh"].view(np.uint32))
+    np.testing.assert_array_equal(it["qh"][:, :F], ref["qh"])
+    assert_rel(host(Y), ref["y"])
