@@ -2,15 +2,17 @@
 
 Default workload: the 2B-class decode step, one token through a 2560 -> 6912
 BitLinear and the 6912 -> 2560 down-projection (ternary weights, 2-bit
-packed; int8 per-token activations).  One step = per-token quantisation of
-the input, the up GEMV with fused dequant, quantisation of the down input,
-the down GEMV with fused dequant.  Weights are packed once before timing (the
-pages describe packing as a one-time conversion).  The timed steps rotate
-over enough distinct copies of the packed weights (> 512 MB) that they
-stream from HBM, not from the 256 MB last-level cache.
+packed; fp32 activations quantised per token to int8).  One step = the up
+BitLinear and the down BitLinear, each one fused launch (per-token absmax
+quantisation, ternary x int8 GEMV, dequant).  Weights are packed once before
+timing (the pages describe packing as a one-time conversion).  The timed
+steps rotate over enough distinct copies of the packed weights (> 512 MB)
+that they stream from HBM, not from the 256 MB last-level cache, and are
+replayed from a HIP graph (launch-bound work; the replay is checked against
+the eager result first).
 
 value = packed-weight bytes of both projections per step / wall time per
-step (GB/s), launch gaps and the quantisation kernels included.
+step (GB/s), every kernel and the gaps between them included.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-extra]
@@ -46,8 +48,8 @@ def parse():
 
 
 def event_time_per_launch(fn, n, torch):
-    """Average duration of fn()'s kernel, from an event pair around each launch
-    on the current stream (the one the binding launches on)."""
+    """Average duration of fn()'s kernel(s), from an event pair around each
+    launch on the current stream (the one the binding launches on)."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
     for i in range(n):
@@ -57,6 +59,37 @@ def event_time_per_launch(fn, n, torch):
     torch.cuda.synchronize()
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return float(np.mean(ms)), float(np.median(ms))
+
+
+def capture(fn, n, torch):
+    """HIP graph of fn(0..n-1) launched back to back on a capture stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn_warm = [fn(i) for i in range(min(n, 2))]  # noqa: F841  (eager warm-up on s)
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def graph_time_per_launch(fn, n, reps, torch):
+    """Average time per fn() inside a replayed graph of n launches, from one
+    event pair around `reps` replays on the replay stream."""
+    g = capture(fn, n, torch)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (n * reps)
 
 
 def main():
@@ -89,52 +122,76 @@ def main():
     copies = max(2, int(np.ceil(600e6 / (2 * pbytes))))
     ups = [Wup.clone() for _ in range(copies)]
     dns = [Wdn.clone() for _ in range(copies)]
-    q1 = B.bitlinear_quant_act(x)
-    q2 = B.bitlinear_quant_act(xd)
+    ws1 = B.fused_workspace(1, K, dev)
+    ws2 = B.fused_workspace(1, N, dev)
     y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
     y2 = torch.empty((1, K), dtype=torch.float32, device=dev)
 
     def step(i):
         j = i % copies
-        B.bitlinear_quant_act(x, out=q1)
-        B.bitlinear_forward(q1[0], q1[1], q1[2], K, ups[j], sup, N, out=y1)
-        B.bitlinear_quant_act(xd, out=q2)
-        B.bitlinear_forward(q2[0], q2[1], q2[2], N, dns[j], sdn, K, out=y2)
+        B.bitlinear_forward_fused(x, ups[j], sup, N, out=y1, ws=ws1)
+        B.bitlinear_forward_fused(xd, dns[j], sdn, K, out=y2, ws=ws2)
 
-    for i in range(args.warmup):
-        step(i)
+    # eager reference of one step, then the graph (one replay = `copies` steps)
+    step(0)
+    torch.cuda.synchronize()
+    ref1, ref2 = y1.clone(), y2.clone()
+    graph = capture(step, copies, torch)
+    for _ in range(3):
+        y1.zero_()
+        y2.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(y1, ref1) and torch.equal(y2, ref2)):
+            raise RuntimeError("graph replay differs from the eager step")
+    reps = max(1, args.steps // copies)
+    wreps = max(1, args.warmup // copies)
+    steps = reps * copies
+    for _ in range(wreps):
+        graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    for _ in range(reps):
+        graph.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = (t1 - t0) * 1e3 / steps
     step_bytes = 2 * pbytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # ---------------- dominant kernel: the up GEMV, per-launch event timing
-    nl = 400
-    up_ms, up_med = event_time_per_launch(
-        lambda i: B.bitlinear_forward(q1[0], q1[1], q1[2], K, ups[i % copies], sup, N, out=y1),
-        nl, torch)
-    alg_up = pbytes + K + 4 + 4 + 4 + N * 4   # W + xq + x_scale + rowsum + w_scale + y
-    dn_ms, dn_med = event_time_per_launch(
-        lambda i: B.bitlinear_forward(q2[0], q2[1], q2[2], N, dns[i % copies], sdn, K, out=y2),
-        nl, torch)
-    alg_dn = pbytes + N + 12 + K * 4
+    # eager (one launch per call from Python), for context
+    for i in range(20):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ne = 2 * copies
+    for i in range(ne):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / ne
+
+    # ---------------- dominant kernel: the fused up GEMV, HIP events around
+    # graph replays of back-to-back launches over the rotating copies
+    up_ms = graph_time_per_launch(
+        lambda i: B.bitlinear_forward_fused(x, ups[i % copies], sup, N, out=y1, ws=ws1),
+        copies, 10, torch)
+    dn_ms = graph_time_per_launch(
+        lambda i: B.bitlinear_forward_fused(xd, dns[i % copies], sdn, K, out=y2, ws=ws2),
+        copies, 10, torch)
+    alg_up = pbytes + K * 4 + 4 + N * 4      # packed W + fp32 x + w_scale + fp32 y
+    alg_dn = pbytes + N * 4 + 4 + K * 4
     achieved = alg_up / (up_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemv_kernel<1,4,0> (2560->6912, M=1)",
-                "avg_us": round(up_ms * 1e3, 3), "median_us": round(up_med * 1e3, 3),
-                "algorithmic_bytes": alg_up}
+                "kernel": "gemv_kernel<1,8,0,1> (fused quant + GEMV, 2560->6912, M=1)",
+                "avg_us": round(up_ms * 1e3, 3), "algorithmic_bytes": alg_up}
     kernels = {
-        "gemv_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3), "GBps": round(achieved, 1)},
-        "gemv_down_6912x2560": {"avg_us": round(dn_ms * 1e3, 3),
-                                "GBps": round(alg_dn / (dn_ms * 1e-3) / 1e9, 1)},
+        "gemv_fused_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3), "GBps": round(achieved, 1)},
+        "gemv_fused_down_6912x2560": {"avg_us": round(dn_ms * 1e3, 3),
+                                      "GBps": round(alg_dn / (dn_ms * 1e-3) / 1e9, 1)},
+        "decode_step_eager_us": round(eager_ms * 1e3, 3),
     }
-    del ups, dns
+    del ups, dns, graph
     torch.cuda.empty_cache()
 
     if not args.no_extra:
@@ -146,20 +203,23 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "steps": steps, "warmup": wreps * copies, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "decode 2B-class: M=1, BitLinear 2560->6912 + 6912->2560, "
-                               "ternary 2-bit packed weights ~N(0,0.02), x ~N(0,1) int8 per token",
+        "config": {"workload": "decode 2B-class: M=1, BitLinear 2560->6912 + 6912->2560 from fp32 "
+                               "activations, ternary 2-bit packed weights ~N(0,0.02), x ~N(0,1), "
+                               "int8 per-token quantisation fused into each GEMV",
                    "M": 1, "K": K, "N": N, "weight_copies": copies,
-                   "step_weight_bytes": step_bytes, "parallelism": "single GPU"},
+                   "step_weight_bytes": step_bytes, "launch": "HIP graph of back-to-back steps",
+                   "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
     print(json.dumps(out), flush=True)
 
 
 def extra_workloads(torch, B, synth, dev):
-    """Kernel timings of the other shapes (prefill GEMM, 100B-class decode, FFN)."""
+    """Kernel timings of the other shapes (prefill GEMM, 100B-class decode, FFN),
+    each from HIP events around graph replays of back-to-back launches."""
     res = {}
     # prefill GEMM: M=2048, K=2560, N=6912
     c = synth.PREFILL_2B
@@ -170,17 +230,15 @@ def extra_workloads(torch, B, synth, dev):
     q = B.bitlinear_quant_act(X)
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
     copies = [Wp.clone() for _ in range(4)]
-    for i in range(5):
-        B.bitlinear_forward(q[0], q[1], q[2], K, copies[i % 4], sc, N, out=Y)
-    ms, med = event_time_per_launch(
-        lambda i: B.bitlinear_forward(q[0], q[1], q[2], K, copies[i % 4], sc, N, out=Y), 50, torch)
+    ms = graph_time_per_launch(
+        lambda i: B.bitlinear_forward(q[0], q[1], q[2], K, copies[i % 4], sc, N, out=Y), 8, 5, torch)
     ops = 2.0 * M * N * K
     res["prefill_gemm_2048x2560x6912"] = {
         "avg_us": round(ms * 1e3, 2), "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
         "frac_int8_peak": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
-    qa_ms, _ = event_time_per_launch(lambda i: B.bitlinear_quant_act(X, out=q), 20, torch)
+    qa_ms = graph_time_per_launch(lambda i: B.bitlinear_quant_act(X, out=q), 8, 5, torch)
     res["act_quant_2048x2560"] = {"avg_us": round(qa_ms * 1e3, 2),
-                                  "GBps": round(M * K * 5 / (qa_ms * 1e-3) / 1e9, 1)}
+                                  "GBps": round(M * (K * 5 + 8) / (qa_ms * 1e-3) / 1e9, 1)}
     del copies, Y, X, q, Wp
     torch.cuda.empty_cache()
 
@@ -196,17 +254,25 @@ def extra_workloads(torch, B, synth, dev):
         ncp = max(2, int(np.ceil(600e6 / pb)))
         cps = [Wp.clone() for _ in range(ncp)]
         for M in (1, 8):
-            q = B.bitlinear_quant_act(torch.from_numpy(p["X"][:M]).to(dev))
+            Xm = torch.from_numpy(p["X"][:M]).to(dev)
+            q = B.bitlinear_quant_act(Xm)
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            for i in range(3):
-                B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y)
-            ms, med = event_time_per_launch(
+            ms = graph_time_per_launch(
                 lambda i: B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y),
-                60, torch)
+                ncp, 5, torch)
             alg = pb + M * (K + 8) + 4 + M * N * 4
             res[f"decode_100b_{tag}_M{M}"] = {
                 "avg_us": round(ms * 1e3, 2), "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
                 "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            if M == 1:
+                wsf = B.fused_workspace(1, K, dev)
+                ms = graph_time_per_launch(
+                    lambda i: B.bitlinear_forward_fused(Xm, cps[i % ncp], sc, N, out=Y, ws=wsf),
+                    ncp, 5, torch)
+                alg = pb + K * 4 + 4 + N * 4
+                res[f"decode_100b_{tag}_M1_fused"] = {
+                    "avg_us": round(ms * 1e3, 2), "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del cps, Wp
         torch.cuda.empty_cache()
     del Wd
@@ -220,6 +286,7 @@ def extra_workloads(torch, B, synth, dev):
     wbytes = sum(pk[0].numel() * 4 for pk in packs)
     ncp = max(2, int(np.ceil(600e6 / wbytes)))
     cps = [[(pk[0].clone(), pk[1]) for pk in packs] for _ in range(ncp)]
+    eps = float(np.finfo(np.float32).eps)
     for M in c["M_list"]:
         H = torch.from_numpy(f["H"][:M]).to(dev)
         ws = torch.empty(B.lib().bitnet_ffn_workspace_bytes(M, D, F), dtype=torch.uint8, device=dev)
@@ -227,12 +294,10 @@ def extra_workloads(torch, B, synth, dev):
 
         def run(i):
             g, u, dn = cps[i % ncp]
-            B.bitnet_ffn_forward(H, None, float(np.finfo(np.float32).eps), g[0], g[1], u[0], u[1],
-                                 dn[0], dn[1], D, F, out=Y, ws=ws)
+            B.bitnet_ffn_forward(H, None, eps, g[0], g[1], u[0], u[1], dn[0], dn[1], D, F,
+                                 out=Y, ws=ws)
 
-        for i in range(3):
-            run(i)
-        ms, med = event_time_per_launch(run, 60, torch)
+        ms = graph_time_per_launch(run, ncp, 5, torch)
         res[f"ffn_2b_M{M}"] = {"avg_us": round(ms * 1e3, 2),
                                "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
                                "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -157,6 +157,28 @@ int bitlinear_forward_kernel(const int8_t *Xq, const float *x_scale, const int32
                              int64_t M, int64_t K, const uint32_t *Wp, const float *w_scale,
                              int64_t N, float *Y, int32_t *acc_out, int kernel, void *stream);
 
+/*
+ * bitlinear_forward_fused -- one BitLinear straight from float activations:
+ * per-token quantisation ([P1] "BitNet b1.58" activation_quant) and the
+ * product with fused dequant in one call.  For M == 1 with Kp <= 16384 this
+ * is a single kernel (every block quantises the token into LDS; identical
+ * bits); otherwise bitlinear_quant_act into the workspace, then
+ * bitlinear_forward.  Results are bit-identical to that two-call sequence.
+ *
+ *  X        [M][K] float32 (BL_F32) or bfloat16 (BL_BF16), device.
+ *  Wp, w_scale, N, Y   as bitlinear_forward.
+ *  ws       >= bitlinear_fused_workspace_bytes(M, K) bytes, 16-byte aligned.
+ *           On return it holds Xq [M][Kp] int8 at offset 0, x_scale [M] float
+ *           at offset bitlinear_fused_workspace_offset(M, K, 1) and x_rowsum
+ *           [M] int32 at offset bitlinear_fused_workspace_offset(M, K, 2).
+ *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP.
+ */
+size_t bitlinear_fused_workspace_bytes(int64_t M, int64_t K);
+size_t bitlinear_fused_workspace_offset(int64_t M, int64_t K, int which);
+int bitlinear_forward_fused(const void *X, int dtype, int64_t M, int64_t K, const uint32_t *Wp,
+                            const float *w_scale, int64_t N, float *Y, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* Workspace layout of bitnet_ffn_forward.  bitnet_ffn_workspace_layout fills
  * off[BL_FFN_WS_COUNT] with byte offsets (each 256-byte aligned) and returns
  * the total size.  After a call the workspace holds the block's internals:

@@ -55,6 +55,12 @@ def lib():
     L.bitlinear_forward.restype = I
     L.bitlinear_forward_kernel.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, I, P]
     L.bitlinear_forward_kernel.restype = I
+    L.bitlinear_fused_workspace_bytes.argtypes = [I64, I64]
+    L.bitlinear_fused_workspace_bytes.restype = SZ
+    L.bitlinear_fused_workspace_offset.argtypes = [I64, I64, I]
+    L.bitlinear_fused_workspace_offset.restype = SZ
+    L.bitlinear_forward_fused.argtypes = [P, I, I64, I64, P, P, I64, P, P, SZ, P]
+    L.bitlinear_forward_fused.restype = I
     L.bitnet_ffn_workspace_layout.argtypes = [I64, I64, I64, P]
     L.bitnet_ffn_workspace_layout.restype = SZ
     L.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
@@ -154,6 +160,45 @@ def bitlinear_forward(Xq, x_scale, x_rowsum, K, Wp, w_scale, N, with_acc=False,
         int(kernel), _stream(dev))
     _check(st, "bitlinear_forward")
     return (Y, acc) if with_acc else Y
+
+
+def _act_dtype(X):
+    if X.dtype == torch.float32:
+        return BL_F32
+    if X.dtype == torch.bfloat16:
+        return BL_BF16
+    raise ValueError("activations must be float32 or bfloat16")
+
+
+def fused_workspace(M, K, device):
+    n = lib().bitlinear_fused_workspace_bytes(int(M), int(K))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def bitlinear_forward_fused(X, Wp, w_scale, N, out=None, ws=None):
+    """One BitLinear from float activations X [M, K] -> Y [M, N] float32.
+
+    Returns (Y, ws); ws holds the int8 codes, scales and row sums (see
+    fused_internals)."""
+    M, K = X.shape
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = ws if ws is not None else fused_workspace(M, K, dev)
+    st = lib().bitlinear_forward_fused(_dev(X, "X"), _act_dtype(X), M, K, _dev(Wp, "Wp"),
+                                       _dev(w_scale, "w_scale"), N, _dev(Y, "Y"), _dev(ws, "ws"),
+                                       ws.numel(), _stream(dev))
+    _check(st, "bitlinear_forward_fused")
+    return Y, ws
+
+
+def fused_internals(ws, M, K):
+    L = lib()
+    kp = padded_k(K)
+    o1 = L.bitlinear_fused_workspace_offset(M, K, 1)
+    o2 = L.bitlinear_fused_workspace_offset(M, K, 2)
+    return {"xq": ws[:M * kp].view(torch.int8).reshape(M, kp),
+            "x_scale": ws[o1:o1 + 4 * M].view(torch.float32),
+            "x_rowsum": ws[o2:o2 + 4 * M].view(torch.int32)}
 
 
 def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=None, ws=None):

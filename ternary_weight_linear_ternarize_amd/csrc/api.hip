@@ -112,6 +112,46 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
                                   BL_KERNEL_AUTO, stream);
 }
 
+size_t bitlinear_fused_workspace_offset(int64_t M, int64_t K, int which) {
+  if (!m_ok(M) || !dim_ok(K)) return 0;
+  const size_t q = up256((size_t)M * (size_t)padk(K));
+  const size_t sc = up256((size_t)M * 4);
+  switch (which) {
+    case 0: return 0;
+    case 1: return q;
+    case 2: return q + sc;
+    default: return q + 2 * sc;
+  }
+}
+
+size_t bitlinear_fused_workspace_bytes(int64_t M, int64_t K) {
+  return bitlinear_fused_workspace_offset(M, K, 3);
+}
+
+int bitlinear_forward_fused(const void* X, int dtype, int64_t M, int64_t K, const uint32_t* Wp,
+                            const float* w_scale, int64_t N, float* Y, void* ws, size_t ws_bytes,
+                            void* stream) {
+  if (!X || !Wp || !w_scale || !Y) return BL_EINVAL;
+  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(K) || !dim_ok(N)) return BL_ESHAPE;
+  if (!ws || ws_bytes < bitlinear_fused_workspace_bytes(M, K)) return BL_EWORKSPACE;
+  if (!aligned(X, dtype == BL_F32 ? 4 : 2) || !aligned(Wp, 16) || !aligned(w_scale, 4) ||
+      !aligned(Y, 4) || !aligned(ws, 16))
+    return BL_EALIGN;
+  char* base = reinterpret_cast<char*>(ws);
+  int8_t* xq = reinterpret_cast<int8_t*>(base);
+  float* xs = reinterpret_cast<float*>(base + bitlinear_fused_workspace_offset(M, K, 1));
+  int32_t* rs = reinterpret_cast<int32_t*>(base + bitlinear_fused_workspace_offset(M, K, 2));
+  hipStream_t s = as_stream(stream);
+  const bool bf16 = dtype == BL_BF16;
+  if (M == 1 && bl::gemv_fused_ok(K))
+    return hip_status(bl::launch_gemv_fused(X, bf16, K, Wp, w_scale, N, Y, nullptr, xq, xs, rs, s));
+  hipError_t e = bl::launch_act_quant(X, bf16, M, K, xq, xs, rs, nullptr, 0, s);
+  if (e != hipSuccess) return BL_EHIP;
+  if (M == 1) return hip_status(bl::launch_gemv(xq, xs, rs, K, Wp, w_scale, N, Y, nullptr, s));
+  return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
+}
+
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off) {
   if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return 0;
   const size_t m = (size_t)M;
@@ -176,6 +216,11 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   else
     e = bl::launch_mfma_gateup(qx, gx, rsx, M, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
   if (e != hipSuccess) return BL_EHIP;
+  if (M == 1 && bl::gemv_fused_ok(F)) {
+    // requantise h inside the down GEMV (scale from the partial maxima)
+    e = bl::launch_gemv_parts(h, ghp, nparts, F, Wd, sd, D, Y, qh, gh, rsh, s);
+    return hip_status(e);
+  }
   e = bl::launch_act_quant(h, false, M, F, qh, gh, rsh, ghp, nparts, s);
   if (e != hipSuccess) return BL_EHIP;
   if (M == 1)

@@ -19,6 +19,14 @@ constexpr float kQ = 127.0f;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of streamed data that is read once (non-temporal hint).
+__device__ __forceinline__ uint4 load_stream_u4(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
@@ -33,13 +41,49 @@ __device__ __forceinline__ float load_act(const void* p, int64_t i) {
   }
 }
 
-// int8 code of x given d = gamma + eps: clamp(rne((x * 127) / d), -127, 127).
+// int8 code of x given d = gamma + eps: clamp(rne((x * 127) / d), -127, 127),
+// with the quotient correctly rounded (IEEE division).
 __device__ __forceinline__ int quant_code(float x, float d) {
   float v = __fmul_rn(x, kQ);
   v = __fdiv_rn(v, d);
   v = __builtin_rintf(v);
   v = fminf(fmaxf(v, -kQ), kQ);
   return (int)v;
+}
+
+// Per-row divisor for quant_code_fast: d = gamma + eps and y = 1/d correctly
+// rounded.  `fast` is false when d is so large that 1/d would leave the normal
+// range; such rows use quant_code.
+struct QuantDiv {
+  float d, y;
+  bool fast;
+};
+__device__ __forceinline__ QuantDiv make_qdiv(float gamma) {
+  QuantDiv q;
+  q.d = __fadd_rn(gamma, kEps);
+  q.y = __fdiv_rn(1.0f, q.d);
+  q.fast = q.d < 0x1p100f;
+  return q;
+}
+
+// Same code as quant_code, with the division done by Markstein's correction
+// (P. Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", 1990): with y = RN(1/d) and q0 = RN(a*y), the
+// residual r = a - q0*d is exact through one fused multiply-add and
+// RN(q0 + r*y) is the correctly rounded a/d.  Valid while d, 1/d and a stay
+// in the normal range (guaranteed for QuantDiv::fast rows, d >= 1e-5).
+__device__ __forceinline__ int quant_code_fast(float x, const QuantDiv& q) {
+  const float a = __fmul_rn(x, kQ);
+  const float q0 = __fmul_rn(a, q.y);
+  const float r = __builtin_fmaf(-q0, q.d, a);
+  float v = __builtin_fmaf(r, q.y, q0);
+  v = __builtin_rintf(v);
+  v = fminf(fmaxf(v, -kQ), kQ);
+  return (int)v;
+}
+
+__device__ __forceinline__ int quant_code_any(float x, const QuantDiv& q) {
+  return q.fast ? quant_code_fast(x, q) : quant_code(x, q.d);
 }
 
 // Dequantised output: ((float)acc * (g_w * g_m)) / 127.
@@ -94,39 +138,47 @@ __device__ double finalize_bins(const uint64_t* bins, unsigned long long* limbs,
   }
   __syncthreads();
   if (tid == 0) {
-    uint32_t w[kLimbs];
+    // carry-propagate into 32-bit words (kept in limbs[], low halves)
     unsigned long long carry = 0ull;
-    for (int i = 0; i < kLimbs; ++i) {
-      unsigned long long t = limbs[i] + carry;
-      w[i] = (uint32_t)t;
-      carry = t >> 32;
-    }
     int top = -1;
-    for (int i = kLimbs - 1; i >= 0; --i) {
-      if (w[i]) { top = i; break; }
+    for (int i = 0; i < kLimbs; ++i) {
+      const unsigned long long t = limbs[i] + carry;
+      limbs[i] = t & 0xffffffffull;
+      carry = t >> 32;
+      if (t & 0xffffffffull) top = i;
     }
     double r = 0.0;
     if (top >= 0) {
-      int p = 32 * top + (31 - __clz((int)w[top]));  // index of the leading bit
-      // bit k of X
-      auto bit = [&](int k) -> uint32_t { return (w[k >> 5] >> (k & 31)) & 1u; };
-      uint64_t mant = 0ull;
-      int lo = p - 52;  // lowest bit kept
-      if (lo <= 0) {
-        for (int k = p; k >= 0; --k) mant = (mant << 1) | bit(k);
-        r = ldexp((double)mant, -149 * SH);
+      const uint32_t wt = (uint32_t)limbs[top];
+      const int p = 32 * top + (31 - __clz((int)wt));  // leading bit of X
+      if (p < 53) {
+        const uint64_t x = limbs[0] | (top >= 1 ? (limbs[1] << 32) : 0ull);
+        r = ldexp((double)x, -149 * SH);  // exact
       } else {
-        for (int k = p; k >= lo; --k) mant = (mant << 1) | bit(k);
-        uint32_t rnd = bit(lo - 1);
-        bool sticky = false;
-        int rb = lo - 1;  // bits strictly below rb
-        for (int i = 0; i < (rb >> 5); ++i) sticky |= (w[i] != 0u);
-        if (rb & 31) sticky |= (w[rb >> 5] & ((1u << (rb & 31)) - 1u)) != 0u;
+        // 64-bit window whose top bit is bit p of X, plus a sticky bit for
+        // everything below the window
+        const int lo = p - 63;
+        uint64_t win;
+        bool below = false;
+        if (lo >= 0) {
+          const int i = lo >> 5, o = lo & 31;
+          const uint64_t t = limbs[i] | (limbs[i + 1] << 32);
+          const uint64_t h = (i + 2 < kLimbs) ? limbs[i + 2] : 0ull;
+          win = o ? ((t >> o) | (h << (64 - o))) : t;
+          for (int j = 0; j < i; ++j) below |= (limbs[j] != 0ull);
+          if (o) below |= (limbs[i] & ((1ull << o) - 1ull)) != 0ull;
+        } else {
+          win = (limbs[0] | (limbs[1] << 32)) << (-lo);
+        }
+        uint64_t mant = win >> 11;                     // 53 bits
+        const bool rnd = (win >> 10) & 1ull;
+        const bool sticky = below || (win & 0x3ffull) != 0ull;
+        int e = p - 52;
         if (rnd && (sticky || (mant & 1ull))) {
           mant += 1ull;
-          if (mant == (1ull << 53)) { mant >>= 1; lo += 1; }
+          if (mant == (1ull << 53)) { mant >>= 1; e += 1; }
         }
-        r = ldexp((double)mant, lo - 149 * SH);
+        r = ldexp((double)mant, e - 149 * SH);
       }
     }
     *result = r;

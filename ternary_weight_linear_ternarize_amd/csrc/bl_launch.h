@@ -29,6 +29,19 @@ hipError_t launch_gemv(const int8_t* Xq, const float* x_scale, const int32_t* ro
                        const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
                        int32_t* acc_out, hipStream_t s);
 
+// One token from float activations: quantise inside the GEMV (every block
+// redoes the row into LDS) -- one launch.  Needs bl_padded_k(K) <= 16384
+// (gemv_fused_ok).  xq_out/xs_out/rs_out (optional) receive the codes.
+bool gemv_fused_ok(int64_t K);
+hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t* Wp,
+                             const float* w_scale, int64_t N, float* Y, int32_t* acc_out,
+                             int8_t* xq_out, float* xs_out, int32_t* rs_out, hipStream_t s);
+// As launch_gemv_fused for a float32 row whose scale is the maximum of
+// gparts[0..nparts) (partial maxima from launch_gemv_gateup).
+hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, int64_t K,
+                             const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
+                             int8_t* xq_out, float* xs_out, int32_t* rs_out, hipStream_t s);
+
 // Y = dequant(Xq . T^T) on MFMA: skinny (M <= 64, tiled == false) or the
 // 128 x 128 tiled kernel.
 hipError_t launch_mfma(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,

@@ -5,21 +5,34 @@
 // Here it is taken in the shifted-code form
 //   acc = sum_k q[k] * (t + 1) - sum_k q[k],
 // so the 2-bit codes (0, 1, 2) feed the 4-wide int8 dot product directly
-// after a mask, and the row sum of q (from the quantiser) removes the shift.
+// after a mask, and the row sum of q removes the shift.
 //
-// Layout of the work: a wave owns R consecutive weight rows; its 64 lanes
-// span K, lane l taking the 64-weight chunks l, l+64, ... (16 bytes of 2-bit
-// codes, one dwordx4 load per row and chunk), so each row is read as one
-// contiguous stream.  The activation chunk of a lane is the same for every
-// row and stays in registers.  The R per-lane partial sums are reduced across
-// the wave with a transposing butterfly (R rows in log2(64) steps), and the
-// epilogue dequantises: y = ((float)acc * (g_w * g_x)) / 127.
+// Work layout: a wave owns R consecutive weight rows; its 64 lanes span K,
+// lane l taking the 64-weight chunks l, l+64, ... (16 bytes of 2-bit codes:
+// one dwordx4 load per row and chunk), so each row is one contiguous stream
+// and a wave-wide load covers up to 1 KiB.  All weight loads of a wave are
+// issued before anything waits on them.  The activation chunk of a lane is
+// the same for every row and stays in registers.  The R per-lane partial sums
+// are reduced across the wave with a transposing butterfly, and the epilogue
+// dequantises: y = ((float)acc * (g_w * g_x)) / 127.
+//
+// Activation sources (XSRC):
+//   XS_INT8  int8 codes, scale and row sum from bitlinear_quant_act;
+//   XS_F32 / XS_BF16  float activations quantised inside the kernel (youngju.dev
+//            "BitNet b1.58" activation_quant: scale = max |x|, codes
+//            rne(x * 127 / (scale + 1e-5))), every block redoing the row
+//            (identical bits) into LDS -- one launch per layer;
+//   XS_PARTS float activations whose scale is the maximum of per-block partial
+//            maxima written by the previous kernel (the FFN's h).
 #include "bl_device.h"
 #include "bl_launch.h"
 
 namespace bl {
 
 enum { EPI_STORE = 0, EPI_GATEUP = 1 };
+enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3 };
+
+constexpr int kFusedMaxKp = 7168;  // largest padded K quantised inside the GEMV
 
 // Reduce v[0..R) (per-lane partials of R rows) across the 64 lanes.  On
 // return lane l holds the full sum of row (l >> (6 - log2 R)) in v[0].
@@ -50,133 +63,295 @@ __device__ __forceinline__ int wave_transpose_reduce(int (&v)[R]) {
   return v[0];
 }
 
-// KC: 64-weight chunks per lane per K segment (a segment is 4096 * KC
-// weights).  R: rows per wave.
-// EPI_STORE: rows n0..n0+R-1 of W -> Y.  EPI_GATEUP: rows n0..n0+R/2-1 of
-// Wg and of Wu -> h = relu(g)^2 * u, plus the block's max |h| into
-// gh_parts[blockIdx.x].
-template <int KC, int R, int EPI>
-__global__ __launch_bounds__(256) void gemv_kernel(
-    const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ rowsum, int64_t Kp, const uint32_t* __restrict__ W0,
-    const float* __restrict__ s0, const uint32_t* __restrict__ W1, const float* __restrict__ s1,
-    int64_t N, float* __restrict__ Y, int32_t* __restrict__ acc_out,
-    float* __restrict__ gh_parts) {
-  constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;  // output rows per wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * RW;
-  const int64_t C = Kp / 64;  // chunks per row
-  const int64_t wpr = Kp / 16;
-
-  int part[R];
+__device__ __forceinline__ float block_max4(float v, float* red) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) part[r] = 0;
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
 
-  // K is walked in segments of 64*KC chunks (one segment when K <= 4096*KC)
-  for (int64_t seg = 0; seg < C; seg += 64 * KC) {
-    // activation chunks of this lane, natural order: 16 x int32 per chunk
-    int x[KC][16];
+__device__ __forceinline__ int block_sum4(int v, int* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+struct GemvArgs {
+  const void* x;            // int8 codes (XS_INT8) or float/bf16 activations
+  const float* x_scale;     // XS_INT8: scale g_x
+  const int32_t* rowsum;    // XS_INT8: row sum of the codes
+  const float* gparts;      // XS_PARTS: partial maxima [nparts]
+  int nparts;
+  int64_t K, Kp;
+  const uint32_t* W0;
+  const float* s0;
+  const uint32_t* W1;       // EPI_GATEUP: up weights
+  const float* s1;
+  int64_t N;
+  float* Y;
+  int32_t* acc_out;         // optional
+  float* gh_parts;          // EPI_GATEUP: per-block max |h|
+  int8_t* xq_out;           // fused: optional copy of the codes (block 0)
+  float* xs_out;            // fused: optional scale
+  int32_t* rs_out;          // fused: optional row sum
+};
+
+// Loads the packed chunks of row block rb (clamped into range: straight-line).
+template <int KC, int R, int EPI>
+__device__ __forceinline__ void gemv_load_w(const GemvArgs& a, int64_t rb, int lane, int C,
+                                            int wpr, uint4 (&w)[R][KC]) {
+  constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t* base = (EPI == EPI_GATEUP && r >= RW) ? a.W1 : a.W0;
+    int64_t n = rb * RW + (r % RW);
+    n = n < a.N ? n : a.N - 1;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-      const int64_t c = seg + lane + 64 * i;
-      if (c < C) {
-        const int4* p = reinterpret_cast<const int4*>(xq + 64 * c);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int4 v = p[q];
-          x[i][4 * q + 0] = v.x; x[i][4 * q + 1] = v.y; x[i][4 * q + 2] = v.z; x[i][4 * q + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) x[i][q] = 0;
-      }
-    }
-
-    // weight chunks: row r of this wave, chunk i
-    uint4 w[R][KC];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t* base;
-      int64_t n;
-      if constexpr (EPI == EPI_GATEUP) {
-        n = n0 + (r % RW);
-        base = (r < RW) ? W0 : W1;
-      } else {
-        n = n0 + r;
-        base = W0;
-      }
-#pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        const int64_t c = seg + lane + 64 * i;
-        if (n < N && c < C)
-          w[r][i] = *reinterpret_cast<const uint4*>(base + n * wpr + 4 * c);
-        else
-          w[r][i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      Dot16 d;
-#pragma unroll
-      for (int i = 0; i < KC; ++i) {
-        d.add(w[r][i].x, x[i][0], x[i][1], x[i][2], x[i][3]);
-        d.add(w[r][i].y, x[i][4], x[i][5], x[i][6], x[i][7]);
-        d.add(w[r][i].z, x[i][8], x[i][9], x[i][10], x[i][11]);
-        d.add(w[r][i].w, x[i][12], x[i][13], x[i][14], x[i][15]);
-      }
-      part[r] += d.total();
+      int c = lane + 64 * i;
+      c = c < C ? c : C - 1;
+      w[r][i] = load_stream_u4(reinterpret_cast<const uint4*>(base + n * wpr) + c);
     }
   }
+}
 
+template <int KC, int R>
+__device__ __forceinline__ void gemv_dots(const uint4 (&w)[R][KC], const int (&x)[KC][16],
+                                          int (&part)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    Dot16 d;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      d.add(w[r][i].x, x[i][0], x[i][1], x[i][2], x[i][3]);
+      d.add(w[r][i].y, x[i][4], x[i][5], x[i][6], x[i][7]);
+      d.add(w[r][i].z, x[i][8], x[i][9], x[i][10], x[i][11]);
+      d.add(w[r][i].w, x[i][12], x[i][13], x[i][14], x[i][15]);
+    }
+    part[r] = d.total();
+  }
+}
+
+// Reduce, dequantise and store the rows of row block rb.  Returns this
+// lane's max |h| contribution (EPI_GATEUP) or 0.
+template <int R, int EPI>
+__device__ __forceinline__ float gemv_epilogue(const GemvArgs& a, int64_t rb, int (&part)[R],
+                                               int rsum, float gx, float sw0, float sw1) {
+  constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;
+  constexpr int LOGR = (R == 1) ? 0 : (R == 2) ? 1 : (R == 4) ? 2 : (R == 8) ? 3 : 4;
+  const int lane = threadIdx.x & 63;
   const int sum = wave_transpose_reduce<R>(part);
-  constexpr int LOGR = (R == 1) ? 0 : (R == 2) ? 1 : (R == 4) ? 2 : 3;
   const int row = lane >> (6 - LOGR);
   const bool leader = (lane & ((64 >> LOGR) - 1)) == 0;
-  const int acc = sum - rowsum[0];
-
+  const int acc = sum - rsum;
+  const int64_t n = rb * RW + row;
   if constexpr (EPI == EPI_STORE) {
-    const int64_t n = n0 + row;
-    if (leader && n < N) {
-      const float sc = __fmul_rn(s0[0], x_scale[0]);
-      Y[n] = dequant(acc, sc);
-      if (acc_out) acc_out[n] = acc;
+    if (leader && n < a.N) {
+      a.Y[n] = dequant(acc, __fmul_rn(sw0, gx));
+      if (a.acc_out) a.acc_out[n] = acc;
     }
+    return 0.0f;
   } else {
     // rows [0, RW) are gate, [RW, R) are up; bring up's sum next to gate's
     constexpr int SPAN = 64 >> LOGR;  // lanes per row
     const int acc_up = __shfl(acc, (lane + RW * SPAN) & 63);
-    float hmax = 0.0f;
-    const int64_t n = n0 + row;
-    if (leader && row < RW && n < N) {
-      const float g = dequant(acc, __fmul_rn(s0[0], x_scale[0]));
-      const float u = dequant(acc_up, __fmul_rn(s1[0], x_scale[0]));
-      const float a = g > 0.0f ? g : 0.0f;
-      const float h = __fmul_rn(__fmul_rn(a, a), u);
-      Y[n] = h;
-      hmax = fabsf(h);
+    float hm = 0.0f;
+    if (leader && row < RW && n < a.N) {
+      const float gv = dequant(acc, __fmul_rn(sw0, gx));
+      const float uv = dequant(acc_up, __fmul_rn(sw1, gx));
+      const float r = gv > 0.0f ? gv : 0.0f;
+      const float h = __fmul_rn(__fmul_rn(r, r), uv);
+      a.Y[n] = h;
+      hm = fabsf(h);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
-    __shared__ float red[4];
-    if (lane == 0) red[wave] = hmax;
-    __syncthreads();
-    if (threadIdx.x == 0)
-      gh_parts[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    return hm;
   }
 }
 
-template <int R, int EPI>
-static hipError_t gemv_dispatch(const int8_t* xq, const float* xs, const int32_t* rs, int64_t Kp,
-                                const uint32_t* W0, const float* s0, const uint32_t* W1,
-                                const float* s1, int64_t N, float* Y, int32_t* acc_out,
-                                float* gh_parts, hipStream_t s) {
+// KC: 64-weight chunks per lane (Kp <= 4096 * KC).  R: weight rows per wave
+// (one row block per wave: every load of the grid is in flight at once, the
+// pattern that measured fastest for both small and large matrices).
+template <int KC, int R, int EPI, int XSRC>
+__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
+  constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;  // output rows per wave
+  constexpr bool FUSED = XSRC != XS_INT8;
+  __shared__ __attribute__((aligned(16))) int8_t xq_lds[FUSED ? 4096 * KC : 16];
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = (int)(a.Kp >> 6);  // 64-weight chunks per row
+  const int wpr = (int)(a.Kp >> 4);
+  const int64_t rb = (int64_t)blockIdx.x * 4 + wave;  // this wave's row block
+
+  uint4 w[R][KC];
+  gemv_load_w<KC, R, EPI>(a, rb, lane, C, wpr, w);
+
+  const float sw0 = a.s0[0];
+  const float sw1 = (EPI == EPI_GATEUP) ? a.s1[0] : 0.0f;
+  float gx = 0.0f;
+  int rsum = 0;
+  int x[KC][16];
+  if constexpr (!FUSED) {
+    gx = a.x_scale[0];
+    rsum = a.rowsum[0];
+    const int8_t* xq = reinterpret_cast<const int8_t*>(a.x);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = lane + 64 * i;
+      const int cc = c < C ? c : C - 1;
+      const int4* p = reinterpret_cast<const int4*>(xq + 64 * cc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int4 v = p[q];
+        if (c >= C) v = make_int4(0, 0, 0, 0);
+        x[i][4 * q + 0] = v.x; x[i][4 * q + 1] = v.y; x[i][4 * q + 2] = v.z; x[i][4 * q + 3] = v.w;
+      }
+    }
+  } else {
+    // quantise the whole row into LDS (every block does the same, same bits)
+    const int K = (int)a.K, nw = (int)(a.Kp >> 2);
+    constexpr int NWT = 4 * KC;  // words per thread: Kp <= 4096 * KC
+    float xv[NWT][4];
+    float g = 0.0f;
+    if constexpr (XSRC == XS_PARTS) {
+      for (int p = tid; p < a.nparts; p += 256) g = fmaxf(g, a.gparts[p]);
+    }
+#pragma unroll
+    for (int j = 0; j < NWT; ++j) {
+      const int wd = tid + 256 * j;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int k = 4 * wd + b;
+        float v = 0.0f;
+        if (wd < nw && k < K) {
+          if constexpr (XSRC == XS_BF16)
+            v = load_act<true>(a.x, k);
+          else
+            v = load_act<false>(a.x, k);
+        }
+        xv[j][b] = v;
+        if constexpr (XSRC != XS_PARTS) g = fmaxf(g, fabsf(v));
+      }
+    }
+    g = block_max4(g, redf);
+    const QuantDiv qd = make_qdiv(g);
+    int rs = 0;
+#pragma unroll
+    for (int j = 0; j < NWT; ++j) {
+      const int wd = tid + 256 * j;
+      if (wd < nw) {
+        uint32_t pk = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int c = quant_code_any(xv[j][b], qd);
+          rs += c;
+          pk |= ((uint32_t)(c & 0xff)) << (8 * b);
+        }
+        reinterpret_cast<uint32_t*>(xq_lds)[wd] = pk;
+        if (blockIdx.x == 0 && a.xq_out) reinterpret_cast<uint32_t*>(a.xq_out)[wd] = pk;
+      }
+    }
+    rsum = block_sum4(rs, redi);  // its barrier also publishes xq_lds
+    gx = g;
+    if (blockIdx.x == 0 && tid == 0) {
+      if (a.xs_out) a.xs_out[0] = g;
+      if (a.rs_out) a.rs_out[0] = rsum;
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = lane + 64 * i;
+      const int cc = c < C ? c : C - 1;
+      const int4* p = reinterpret_cast<const int4*>(xq_lds + 64 * cc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int4 v = p[q];
+        if (c >= C) v = make_int4(0, 0, 0, 0);
+        x[i][4 * q + 0] = v.x; x[i][4 * q + 1] = v.y; x[i][4 * q + 2] = v.z; x[i][4 * q + 3] = v.w;
+      }
+    }
+  }
+
+  int part[R];
+  gemv_dots<KC, R>(w, x, part);
+  float hmax = 0.0f;
+  if (rb * RW < a.N) hmax = gemv_epilogue<R, EPI>(a, rb, part, rsum, gx, sw0, sw1);
+
+  if constexpr (EPI == EPI_GATEUP) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+    __shared__ float redh[4];
+    if (lane == 0) redh[wave] = hmax;
+    __syncthreads();
+    if (tid == 0) a.gh_parts[blockIdx.x] = fmaxf(fmaxf(redh[0], redh[1]), fmaxf(redh[2], redh[3]));
+  }
+}
+
+// K beyond 4096 * 4 weights (int8 codes only): one row block per wave, K
+// walked in segments of 16384 weights.
+template <int R>
+__global__ __launch_bounds__(256) void gemv_long_kernel(const GemvArgs a) {
+  constexpr int KC = 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = (int)(a.Kp >> 6);
+  const int wpr = (int)(a.Kp >> 4);
+  const int64_t rb = (int64_t)blockIdx.x * 4 + wave;
+  const int8_t* xq = reinterpret_cast<const int8_t*>(a.x);
+  const float gx = a.x_scale[0];
+  const int rsum = a.rowsum[0];
+  int total[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) total[r] = 0;
+  for (int seg = 0; seg < C; seg += 64 * KC) {
+    uint4 w[R][KC];
+    int x[KC][16];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t n = rb * R + r;
+      n = n < a.N ? n : a.N - 1;
+#pragma unroll
+      for (int i = 0; i < KC; ++i) {
+        int c = seg + lane + 64 * i;
+        c = c < C ? c : C - 1;
+        w[r][i] = load_stream_u4(reinterpret_cast<const uint4*>(a.W0 + n * wpr) + c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = seg + lane + 64 * i;
+      const int cc = c < C ? c : C - 1;
+      const int4* p = reinterpret_cast<const int4*>(xq + 64 * cc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int4 v = p[q];
+        if (c >= C) v = make_int4(0, 0, 0, 0);
+        x[i][4 * q + 0] = v.x; x[i][4 * q + 1] = v.y; x[i][4 * q + 2] = v.z; x[i][4 * q + 3] = v.w;
+      }
+    }
+    int part[R];
+    gemv_dots<KC, R>(w, x, part);
+#pragma unroll
+    for (int r = 0; r < R; ++r) total[r] += part[r];
+  }
+  if (rb * R < a.N) gemv_epilogue<R, EPI_STORE>(a, rb, total, rsum, gx, a.s0[0], 0.0f);
+}
+
+template <int R, int EPI, int XSRC>
+static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;
-  const int64_t C = Kp / 64;
-  const unsigned blocks = (unsigned)((N + 4 * RW - 1) / (4 * RW));
-#define BL_GEMV_CASE(KCV)                                                                     \
-  hipLaunchKernelGGL((gemv_kernel<KCV, R, EPI>), dim3(blocks), dim3(256), 0, s, xq, xs, rs, Kp, \
-                     W0, s0, W1, s1, N, Y, acc_out, gh_parts)
+  const int64_t C = a.Kp / 64;
+  const int64_t nrb = (a.N + RW - 1) / RW;
+  const unsigned blocks = (unsigned)((nrb + 3) / 4);
+  if (C > 256) {
+    if (XSRC != XS_INT8 || EPI != EPI_STORE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemv_long_kernel<R>), dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+#define BL_GEMV_CASE(KCV) \
+  hipLaunchKernelGGL((gemv_kernel<KCV, R, EPI, XSRC>), dim3(blocks), dim3(256), 0, s, a)
   if (C <= 64) BL_GEMV_CASE(1);
   else if (C <= 128) BL_GEMV_CASE(2);
   else if (C <= 192) BL_GEMV_CASE(3);
@@ -185,23 +360,76 @@ static hipError_t gemv_dispatch(const int8_t* xq, const float* xs, const int32_t
   return hipGetLastError();
 }
 
+static GemvArgs base_args(int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y) {
+  GemvArgs a = {};
+  a.K = K;
+  a.Kp = (K + 63) / 64 * 64;
+  a.W0 = Wp;
+  a.s0 = ws;
+  a.N = N;
+  a.Y = Y;
+  return a;
+}
+
 hipError_t launch_gemv(const int8_t* xq, const float* xs, const int32_t* rs, int64_t K,
                        const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                        int32_t* acc_out, hipStream_t s) {
-  const int64_t Kp = (K + 63) / 64 * 64;
-  return gemv_dispatch<4, EPI_STORE>(xq, xs, rs, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
-                                     nullptr, s);
+  GemvArgs a = base_args(K, Wp, ws, N, Y);
+  a.x = xq;
+  a.x_scale = xs;
+  a.rowsum = rs;
+  a.acc_out = acc_out;
+  return gemv_dispatch<4, EPI_STORE, XS_INT8>(a, s);
 }
 
-int64_t gemv_gateup_parts(int64_t N) { return (N + 7) / 8; }
+// The fused kernels redo the row's quantisation in every block; past ~7K
+// inputs that redundant work costs more than a separate quantisation launch.
+bool gemv_fused_ok(int64_t K) { return (K + 63) / 64 * 64 <= kFusedMaxKp; }
+
+hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t* Wp,
+                             const float* ws, int64_t N, float* Y, int32_t* acc_out,
+                             int8_t* xq_out, float* xs_out, int32_t* rs_out, hipStream_t s) {
+  GemvArgs a = base_args(K, Wp, ws, N, Y);
+  a.x = X;
+  a.acc_out = acc_out;
+  a.xq_out = xq_out;
+  a.xs_out = xs_out;
+  a.rs_out = rs_out;
+  return bf16 ? gemv_dispatch<8, EPI_STORE, XS_BF16>(a, s)
+              : gemv_dispatch<8, EPI_STORE, XS_F32>(a, s);
+}
+
+hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, int64_t K,
+                             const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                             int8_t* xq_out, float* xs_out, int32_t* rs_out, hipStream_t s) {
+  GemvArgs a = base_args(K, Wp, ws, N, Y);
+  a.x = X;
+  a.gparts = gparts;
+  a.nparts = nparts;
+  a.xq_out = xq_out;
+  a.xs_out = xs_out;
+  a.rs_out = rs_out;
+  return gemv_dispatch<8, EPI_STORE, XS_PARTS>(a, s);
+}
+
+constexpr int kGateupR = 4;  // weight rows per wave in the gate/up GEMV (half gate, half up)
+
+// one partial maximum per block: 4 waves x kGateupR/2 output rows
+int64_t gemv_gateup_parts(int64_t N) { return (N + 2 * kGateupR - 1) / (2 * kGateupR); }
 
 hipError_t launch_gemv_gateup(const int8_t* xq, const float* xs, const int32_t* rs, int64_t K,
                               const uint32_t* Wg, const float* sg, const uint32_t* Wu,
                               const float* su, int64_t N, float* H, float* gh_parts,
                               int* nparts, hipStream_t s) {
-  const int64_t Kp = (K + 63) / 64 * 64;
+  GemvArgs a = base_args(K, Wg, sg, N, H);
+  a.x = xq;
+  a.x_scale = xs;
+  a.rowsum = rs;
+  a.W1 = Wu;
+  a.s1 = su;
+  a.gh_parts = gh_parts;
   *nparts = (int)gemv_gateup_parts(N);
-  return gemv_dispatch<4, EPI_GATEUP>(xq, xs, rs, Kp, Wg, sg, Wu, su, N, H, nullptr, gh_parts, s);
+  return gemv_dispatch<kGateupR, EPI_GATEUP, XS_INT8>(a, s);
 }
 
 }  // namespace bl

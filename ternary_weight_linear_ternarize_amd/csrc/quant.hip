@@ -40,7 +40,8 @@ __device__ __forceinline__ int block_sum(int v, int* red) {
 // Writes the int8 codes of row values f(k) (k < K; 0 beyond) into q[0..Kp)
 // and returns this thread's share of their sum.
 template <typename F>
-__device__ __forceinline__ int write_codes(F f, int64_t K, int64_t Kp, float d, int8_t* q) {
+__device__ __forceinline__ int write_codes(F f, int64_t K, int64_t Kp, const QuantDiv& d,
+                                           int8_t* q) {
   int rs = 0;
   uint32_t* q32 = reinterpret_cast<uint32_t*>(q);
   for (int64_t w = threadIdx.x; w < Kp / 4; w += blockDim.x) {
@@ -49,7 +50,7 @@ __device__ __forceinline__ int write_codes(F f, int64_t K, int64_t Kp, float d, 
     for (int b = 0; b < 4; ++b) {
       const int64_t k = 4 * w + b;
       int c = 0;
-      if (k < K) c = quant_code(f(k), d);
+      if (k < K) c = quant_code_any(f(k), d);
       rs += c;
       packed |= ((uint32_t)(c & 0xff)) << (8 * b);
     }
@@ -58,7 +59,55 @@ __device__ __forceinline__ int write_codes(F f, int64_t K, int64_t Kp, float d, 
   return rs;
 }
 
-template <bool BF16>
+// Loads words tid, tid+256, ... (four consecutive elements each) of a row
+// into registers; elements past K read as 0.
+template <bool BF16, int NWT>
+__device__ __forceinline__ void load_row_words(const char* base, int64_t K, int64_t nw,
+                                               float (&xv)[NWT][4]) {
+  const int tid = threadIdx.x;
+  const bool vec = !BF16 && (K & 3) == 0;
+#pragma unroll
+  for (int j = 0; j < NWT; ++j) {
+    const int64_t wd = tid + 256 * j;
+    if (vec && 4 * wd + 3 < K) {
+      const float4 v = *reinterpret_cast<const float4*>(base + 16 * wd);
+      xv[j][0] = v.x; xv[j][1] = v.y; xv[j][2] = v.z; xv[j][3] = v.w;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t k = 4 * wd + b;
+        xv[j][b] = (wd < nw && k < K) ? load_act<BF16>(base, k) : 0.0f;
+      }
+    }
+  }
+}
+
+// Writes the codes of the register-held row words and returns this thread's
+// share of their sum.
+template <int NWT>
+__device__ __forceinline__ int store_row_codes(const float (&xv)[NWT][4], int64_t nw,
+                                               const QuantDiv& d, int8_t* q) {
+  int rs = 0;
+#pragma unroll
+  for (int j = 0; j < NWT; ++j) {
+    const int64_t wd = threadIdx.x + 256 * j;
+    if (wd < nw) {
+      uint32_t pk = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c = quant_code_any(xv[j][b], d);
+        rs += c;
+        pk |= ((uint32_t)(c & 0xff)) << (8 * b);
+      }
+      reinterpret_cast<uint32_t*>(q)[wd] = pk;
+    }
+  }
+  return rs;
+}
+
+// NWT > 0: the row (Kp <= 1024 * NWT) is held in registers and read once.
+// NWT == 0: any length, the row is read twice.
+template <bool BF16, int NWT>
 __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ X, int64_t K,
                                                         int64_t Kp, int8_t* __restrict__ Xq,
                                                         float* __restrict__ x_scale,
@@ -72,12 +121,27 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
   float g = 0.0f;
   if (gamma_parts) {
     for (int p = threadIdx.x; p < nparts; p += blockDim.x) g = fmaxf(g, gamma_parts[(int64_t)p * M + m]);
-  } else {
-    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) g = fmaxf(g, fabsf(load_act<BF16>(base, k)));
   }
-  g = block_max(g, redf);
-  const float d = __fadd_rn(g, kEps);
-  int rs = write_codes([&](int64_t k) { return load_act<BF16>(base, k); }, K, Kp, d, Xq + m * Kp);
+  int rs;
+  if constexpr (NWT > 0) {
+    float xv[NWT][4];
+    load_row_words<BF16, NWT>(base, K, Kp / 4, xv);
+    if (!gamma_parts) {
+#pragma unroll
+      for (int j = 0; j < NWT; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) g = fmaxf(g, fabsf(xv[j][b]));
+    }
+    g = block_max(g, redf);
+    rs = store_row_codes<NWT>(xv, Kp / 4, make_qdiv(g), Xq + m * Kp);
+  } else {
+    if (!gamma_parts) {
+      for (int64_t k = threadIdx.x; k < K; k += blockDim.x) g = fmaxf(g, fabsf(load_act<BF16>(base, k)));
+    }
+    g = block_max(g, redf);
+    rs = write_codes([&](int64_t k) { return load_act<BF16>(base, k); }, K, Kp, make_qdiv(g),
+                     Xq + m * Kp);
+  }
   rs = block_sum(rs, redi);
   if (threadIdx.x == 0) {
     x_scale[m] = g;
@@ -87,11 +151,14 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
 
 // RMSNorm(D) of one row, then its int8 codes.  xn = (x * r) * w with
 // r = 1 / sqrt(ms + eps), ms = binary32(binary64(exact sum x^2) / D).
-template <bool BF16>
+// NWT > 0: the row (Dp <= 1024 * NWT) is held in registers; NWT == 0: any
+// length, the row is re-read from memory for each pass.
+template <bool BF16, int NWT>
 __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
     const void* __restrict__ H, int64_t D, int64_t Dp, const float* __restrict__ norm_w,
     float eps, float* __restrict__ xn, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     int32_t* __restrict__ rowsum) {
+  constexpr int NR = NWT > 0 ? NWT : 1;
   __shared__ unsigned long long bins[4][kBins];
   __shared__ uint64_t tot[kBins];
   __shared__ unsigned long long limbs[kLimbs];
@@ -101,13 +168,24 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t m = blockIdx.x;
   const char* base = reinterpret_cast<const char*>(H) + m * D * (BF16 ? 2 : 4);
+  const int64_t nw = Dp / 4;
+  float xv[NR][4];
+  if constexpr (NWT > 0) load_row_words<BF16, NWT>(base, D, nw, xv);
   for (int i = tid; i < 4 * kBins; i += 256) (&bins[0][0])[i] = 0ull;
   __syncthreads();
-  for (int64_t k = tid; k < D; k += 256) {
-    int b;
+  auto add_bin = [&](float v) {
+    int bb;
     uint32_t mm;
-    bin_of(load_act<BF16>(base, k), b, mm);
-    if (mm) atomicAdd(&bins[wave][b], (unsigned long long)mm * (unsigned long long)mm);
+    bin_of(v, bb, mm);
+    if (mm) atomicAdd(&bins[wave][bb], (unsigned long long)mm * (unsigned long long)mm);
+  };
+  if constexpr (NWT > 0) {
+#pragma unroll
+    for (int j = 0; j < NWT; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) add_bin(xv[j][b]);
+  } else {
+    for (int64_t k = tid; k < D; k += 256) add_bin(load_act<BF16>(base, k));
   }
   __syncthreads();
   for (int b = tid; b < kBins; b += 256) tot[b] = bins[0][b] + bins[1][b] + bins[2][b] + bins[3][b];
@@ -117,19 +195,38 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   // __builtin_sqrtf is correctly rounded under -fhip-fp32-correctly-rounded-divide-sqrt
   // (the __fsqrt_rn intrinsic maps to a native approximation on this toolchain).
   const float r = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(ms, eps)));
-  auto norm = [&](int64_t k) {
-    float v = __fmul_rn(load_act<BF16>(base, k), r);
+  auto norm = [&](float x, int64_t k) {
+    const float v = __fmul_rn(x, r);
     return norm_w ? __fmul_rn(v, norm_w[k]) : v;
   };
   float g = 0.0f;
-  for (int64_t k = tid; k < D; k += 256) {
-    const float v = norm(k);
-    xn[m * D + k] = v;
-    g = fmaxf(g, fabsf(v));
+  int rs;
+  if constexpr (NWT > 0) {
+#pragma unroll
+    for (int j = 0; j < NWT; ++j) {
+      const int64_t wd = tid + 256 * j;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t k = 4 * wd + b;
+        const bool in = wd < nw && k < D;
+        const float v = in ? norm(xv[j][b], k) : 0.0f;
+        xv[j][b] = v;
+        if (in) xn[m * D + k] = v;
+        g = fmaxf(g, fabsf(v));
+      }
+    }
+    g = block_max(g, redf);
+    rs = store_row_codes<NWT>(xv, nw, make_qdiv(g), Xq + m * Dp);
+  } else {
+    for (int64_t k = tid; k < D; k += 256) {
+      const float v = norm(load_act<BF16>(base, k), k);
+      xn[m * D + k] = v;
+      g = fmaxf(g, fabsf(v));
+    }
+    g = block_max(g, redf);
+    rs = write_codes([&](int64_t k) { return norm(load_act<BF16>(base, k), k); }, D, Dp,
+                     make_qdiv(g), Xq + m * Dp);
   }
-  g = block_max(g, redf);
-  const float d = __fadd_rn(g, kEps);
-  int rs = write_codes(norm, D, Dp, d, Xq + m * Dp);
   rs = block_sum(rs, redi);
   if (tid == 0) {
     x_scale[m] = g;
@@ -137,29 +234,51 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   }
 }
 
+template <int NWT>
+static void act_quant_go(const void* X, bool bf16, int64_t M, int64_t K, int64_t Kp, int8_t* Xq,
+                         float* x_scale, int32_t* rowsum, const float* gamma_parts, int nparts,
+                         hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((act_quant_kernel<true, NWT>), dim3((unsigned)M), dim3(256), 0, s, X, K, Kp,
+                       Xq, x_scale, rowsum, gamma_parts, nparts, M);
+  else
+    hipLaunchKernelGGL((act_quant_kernel<false, NWT>), dim3((unsigned)M), dim3(256), 0, s, X, K, Kp,
+                       Xq, x_scale, rowsum, gamma_parts, nparts, M);
+}
+
 hipError_t launch_act_quant(const void* X, bool bf16, int64_t M, int64_t K, int8_t* Xq,
                             float* x_scale, int32_t* rowsum, const float* gamma_parts,
                             int nparts, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (bf16)
-    hipLaunchKernelGGL(act_quant_kernel<true>, dim3((unsigned)M), dim3(256), 0, s, X, K, Kp, Xq,
-                       x_scale, rowsum, gamma_parts, nparts, M);
-  else
-    hipLaunchKernelGGL(act_quant_kernel<false>, dim3((unsigned)M), dim3(256), 0, s, X, K, Kp, Xq,
-                       x_scale, rowsum, gamma_parts, nparts, M);
+  if (Kp <= 1024) act_quant_go<1>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
+  else if (Kp <= 3072) act_quant_go<3>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
+  else if (Kp <= 8192) act_quant_go<8>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
+  else if (Kp <= 16384) act_quant_go<16>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
+  else act_quant_go<0>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
   return hipGetLastError();
+}
+
+template <int NWT>
+static void rmsnorm_go(const void* H, bool bf16, int64_t M, int64_t D, int64_t Dp,
+                       const float* norm_w, float eps, float* xn, int8_t* Xq, float* x_scale,
+                       int32_t* rowsum, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<true, NWT>), dim3((unsigned)M), dim3(256), 0, s, H, D,
+                       Dp, norm_w, eps, xn, Xq, x_scale, rowsum);
+  else
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<false, NWT>), dim3((unsigned)M), dim3(256), 0, s, H, D,
+                       Dp, norm_w, eps, xn, Xq, x_scale, rowsum);
 }
 
 hipError_t launch_rmsnorm_quant(const void* H, bool bf16, int64_t M, int64_t D,
                                 const float* norm_w, float eps, float* xn, int8_t* Xq,
                                 float* x_scale, int32_t* rowsum, hipStream_t s) {
   const int64_t Dp = (D + 63) / 64 * 64;
-  if (bf16)
-    hipLaunchKernelGGL(rmsnorm_quant_kernel<true>, dim3((unsigned)M), dim3(256), 0, s, H, D, Dp,
-                       norm_w, eps, xn, Xq, x_scale, rowsum);
-  else
-    hipLaunchKernelGGL(rmsnorm_quant_kernel<false>, dim3((unsigned)M), dim3(256), 0, s, H, D, Dp,
-                       norm_w, eps, xn, Xq, x_scale, rowsum);
+  if (Dp <= 1024) rmsnorm_go<1>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
+  else if (Dp <= 3072) rmsnorm_go<3>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
+  else if (Dp <= 8192) rmsnorm_go<8>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
+  else if (Dp <= 16384) rmsnorm_go<16>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
+  else rmsnorm_go<0>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
   return hipGetLastError();
 }
 

@@ -240,7 +240,7 @@ def test_ffn_2b_bf16_random_norm(M):
     _ffn_case(M, True, "random")
 
 
-@pytest.mark.parametrize("M,D,F", [(1, 300, 700), (2, 64, 128), (17, 512, 1000), (100, 256, 520),
+@pytest.mark.parametrize("M,D,F", [(1, 300, 700), (2, 64, 128), (2, 17000, 100), (17, 512, 1000), (100, 256, 520),
                                    (256, 512, 1024)])
 def test_ffn_ragged_shapes(M, D, F):
     s = 500 + M
@@ -262,3 +262,28 @@ def test_ffn_ragged_shapes(M, D, F):
     np.testing.assert_array_equal(it["gh"].view(np.uint32), ref["gh"].view(np.uint32))
     np.testing.assert_array_equal(it["qh"][:, :F], ref["qh"])
     assert_rel(host(Y), ref["y"])
+
+
+@pytest.mark.parametrize("M,K,N,bf16", [(1, 2560, 6912, False), (1, 6912, 2560, True),
+                                        (1, 1, 5, False), (1, 16384, 33, False), (1, 16448, 40, False),
+                                        (1, 8192, 300, True), (3, 700, 130, False), (80, 512, 200, True)])
+def test_forward_fused_from_float(M, K, N, bf16):
+    d = synth.random_case(3000 + K + N, M, K, N)
+    X = synth.with_outliers(d["X"], synth.outlier_columns(3000 + K, K)) if K > 100 else d["X"]
+    g, t, Wp, sc = check_pack(d["W"])
+    xd = to_dev(X)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        X = xd.float().cpu().numpy()
+    q, gx, rs = oracle.act_quant(X)
+    acc = oracle.int_linear(q, t)
+    y = oracle.dequant(acc, gx, g)
+    Y, ws = B.bitlinear_forward_fused(xd, Wp, sc, N)
+    it = {k: host(v) for k, v in B.fused_internals(ws, M, K).items()}
+    np.testing.assert_array_equal(it["xq"][:, :K], q)
+    assert not it["xq"][:, K:].any()
+    np.testing.assert_array_equal(it["x_scale"].view(np.uint32), gx.view(np.uint32))
+    np.testing.assert_array_equal(it["x_rowsum"], rs)
+    assert_rel(host(Y), y)
+    Y2, _ = B.bitlinear_forward_fused(xd, Wp, sc, N)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
