@@ -44,7 +44,85 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "ffn", "copy"],
+                    help="run one workload's kernels eagerly --steps times and exit "
+                         "(for profilers); prints a short JSON line")
     return ap.parse_args()
+
+
+def only_workload(args):
+    """Eager launches of one workload (rotating weight copies), for rocprofv3."""
+    import torch
+    from ternary_weight_linear_ternarize_amd import binding as B
+    from ternary_weight_linear_ternarize_amd import synth
+    dev = torch.device("cuda:0")
+    B.lib()
+    n = args.steps
+    if args.only == "copy":
+        a = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)  # 256 MiB
+        b = torch.empty_like(a)
+        for _ in range(n):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        return {"only": "copy", "bytes_per_launch": a.numel() * 4, "launches": n}
+    if args.only == "decode":
+        d = synth.decode_2b()
+        K, N = synth.DECODE_2B["K"], synth.DECODE_2B["N"]
+        Wup, sup = B.bitlinear_pack(torch.from_numpy(d["W_up"]).to(dev))
+        Wdn, sdn = B.bitlinear_pack(torch.from_numpy(d["W_down"]).to(dev))
+        copies = max(2, int(np.ceil(600e6 / (2 * Wup.numel() * 4))))
+        ups = [Wup.clone() for _ in range(copies)]
+        dns = [Wdn.clone() for _ in range(copies)]
+        x = torch.from_numpy(d["x"]).to(dev)
+        xd = torch.from_numpy(d["x_d"]).to(dev)
+        ws1, ws2 = B.fused_workspace(1, K, dev), B.fused_workspace(1, N, dev)
+        y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+        y2 = torch.empty((1, K), dtype=torch.float32, device=dev)
+        for i in range(n):
+            B.bitlinear_forward_fused(x, ups[i % copies], sup, N, out=y1, ws=ws1)
+            B.bitlinear_forward_fused(xd, dns[i % copies], sdn, K, out=y2, ws=ws2)
+    elif args.only == "prefill":
+        c = synth.PREFILL_2B
+        M, K, N = c["M"], c["K"], c["N"]
+        p = synth.prefill_2b()
+        Wp, sc = B.bitlinear_pack(torch.from_numpy(p["W"]).to(dev))
+        q = B.bitlinear_quant_act(torch.from_numpy(p["X"]).to(dev))
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        cps = [Wp.clone() for _ in range(4)]
+        for i in range(n):
+            B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % 4], sc, N, out=Y)
+    elif args.only == "decode100b":
+        c = synth.DECODE_100B
+        K, N = c["K"], c["N"]
+        p = synth.decode_100b()
+        Wp, sc = B.bitlinear_pack(torch.from_numpy(p["W"]).to(dev))
+        del p["W"]
+        ncp = max(2, int(np.ceil(600e6 / (Wp.numel() * 4))))
+        cps = [Wp.clone() for _ in range(ncp)]
+        for M in (1, 8):
+            q = B.bitlinear_quant_act(torch.from_numpy(p["X"][:M]).to(dev))
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            for i in range(n):
+                B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y)
+    elif args.only == "ffn":
+        c = synth.FFN_2B
+        D, F = c["D"], c["F"]
+        f = synth.ffn_2b()
+        packs = [B.bitlinear_pack(torch.from_numpy(f[k]).to(dev)) for k in ("W_gate", "W_up", "W_down")]
+        wbytes = sum(pk[0].numel() * 4 for pk in packs)
+        ncp = max(2, int(np.ceil(600e6 / wbytes)))
+        cps = [[(pk[0].clone(), pk[1]) for pk in packs] for _ in range(ncp)]
+        eps = float(np.finfo(np.float32).eps)
+        for M in c["M_list"]:
+            H = torch.from_numpy(f["H"][:M]).to(dev)
+            ws = torch.empty(B.lib().bitnet_ffn_workspace_bytes(M, D, F), dtype=torch.uint8, device=dev)
+            Y = torch.empty((M, D), dtype=torch.float32, device=dev)
+            for i in range(n):
+                g, u, dn = cps[i % ncp]
+                B.bitnet_ffn_forward(H, None, eps, g[0], g[1], u[0], u[1], dn[0], dn[1], D, F,
+                                     out=Y, ws=ws)
+    torch.cuda.synchronize()
+    return {"only": args.only, "launches_per_shape": n}
 
 
 def event_time_per_launch(fn, n, torch):
@@ -98,6 +176,9 @@ def main():
         print(f"bench.py: only one GPU is supported in this build (asked for {args.gpus}); "
               "the multi-GPU split is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        print(json.dumps(only_workload(args)), flush=True)
+        return
 
     import torch
     from ternary_weight_linear_ternarize_amd import binding as B

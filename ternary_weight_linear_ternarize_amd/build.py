@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
 
 SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip"]
-HEADERS = ["bl_device.h", "bl_launch.h"]
+HEADERS = ["bl_device.h", "bl_launch.h", "gemm_tiles.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

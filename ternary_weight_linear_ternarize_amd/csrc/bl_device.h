@@ -20,6 +20,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte load of streamed data that is read once (non-temporal hint).
 __device__ __forceinline__ uint4 load_stream_u4(const uint4* p) {
@@ -86,9 +87,22 @@ __device__ __forceinline__ int quant_code_any(float x, const QuantDiv& q) {
   return q.fast ? quant_code_fast(x, q) : quant_code(x, q.d);
 }
 
-// Dequantised output: ((float)acc * (g_w * g_m)) / 127.
+// Dequantised output: ((float)acc * (g_w * g_m)) / 127, s = g_w * g_m.
 __device__ __forceinline__ float dequant(int acc, float s) {
   return __fdiv_rn(__fmul_rn((float)acc, s), kQ);
+}
+
+// The same value with the division by 127 done by Markstein's correction
+// from the correctly rounded reciprocal (exact while p / 127 stays normal;
+// smaller products take the IEEE division).
+constexpr float kInvQ = 1.0f / 127.0f;  // RN(1/127), folded at compile time
+__device__ __forceinline__ float dequant_fast(int acc, float s) {
+  const float p = __fmul_rn((float)acc, s);
+  const float q0 = __fmul_rn(p, kInvQ);
+  const float r = __builtin_fmaf(-q0, kQ, p);
+  float q = __builtin_fmaf(r, kInvQ, q0);
+  if (__builtin_expect(fabsf(p) < 0x1p-100f, 0)) q = __fdiv_rn(p, kQ);
+  return q;
 }
 
 // ---------------------------------------------------------------------------

@@ -26,10 +26,15 @@
 // 16(4g+s) .. +15) and the matching 16 activation bytes at offset 64g + 16s.
 #include "bl_device.h"
 #include "bl_launch.h"
+#include "gemm_tiles.h"
 
 namespace bl {
 
 enum { MF_STORE = 0, MF_GATEUP = 1 };
+
+hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                         int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                         int32_t* acc_out, hipStream_t s);
 
 constexpr int kChunk = 256;         // K per chunk
 constexpr int kLdsPitch = 256 + 16; // bytes per staged activation row
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
           const int64_t n = n0 + 16 * (wn * TN + tn) + li;
           if (n < N) {
             const int a = acc[0][tm][tn][r] - rsm;
-            Y[m * N + n] = dequant(a, sc);
+            Y[m * N + n] = dequant_fast(a, sc);
             if (acc_out) acc_out[m * N + n] = a;
           }
         }
@@ -213,8 +218,8 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
           for (int tn = 0; tn < TN; ++tn) {
             const int64_t n = n0 + 16 * (wn * TN + tn) + li;
             if (n < N) {
-              const float gv = dequant(acc[0][tm][tn][r] - rsm, scg);
-              const float uv = dequant(acc[1][tm][tn][r] - rsm, scu);
+              const float gv = dequant_fast(acc[0][tm][tn][r] - rsm, scg);
+              const float uv = dequant_fast(acc[1][tm][tn][r] - rsm, scu);
               const float a = gv > 0.0f ? gv : 0.0f;
               const float h = __fmul_rn(__fmul_rn(a, a), uv);
               Y[m * N + n] = h;
@@ -258,9 +263,7 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        const uint32_t* Wp, const float* ws, int64_t N, float* Y, int32_t* acc_out,
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (tiled || M > 64)
-    return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
-                                             acc_out, nullptr, nullptr, s);
+  if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
@@ -296,6 +299,22 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
                                               gh_parts, nparts, s);
   return mfma_launch<4, 4, 2, 2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                             gh_parts, nparts, s);
+}
+
+}  // namespace bl
+
+namespace bl {
+
+hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                         int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                         int32_t* acc_out, hipStream_t s) {
+  constexpr int TM = 4, TN = 2, WM = 1, WN = 4, KCH = 256;
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  const int64_t Kp = (K + 63) / 64 * 64;
+  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((mfma32_gemm_kernel<TM, TN, WM, WN, KCH>), dim3((unsigned)(nbm * nbn)), dim3(256),
+                     0, s, Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, (int)nbm, (int)nbn);
+  return hipGetLastError();
 }
 
 }  // namespace bl

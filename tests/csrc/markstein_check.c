@@ -42,6 +42,24 @@ int main(int argc, char **argv) {
         float q1 = fmaf(r, y, q0);
         if (q1 != a / d) ++bad;
     }
+    /* division by the constant 127 (dequantisation), products over the
+     * normal range handled by the fast path (|p| >= 2^-100) */
+    const float d127 = 127.0f, y127 = 1.0f / 127.0f;
+    for (long i = 0; i < n; ++i) {
+        float p = ldexpf(1.0f + unit(), (int)(next() % 227) - 100); /* 2^-100 .. 2^127 */
+        if (i & 2) p = -p;
+        if (i & 1) { /* near k + 1/2 multiples of 127 ulps: random low bits */
+            uint32_t u;
+            memcpy(&u, &p, 4);
+            u ^= (uint32_t)(next() & 0xff);
+            memcpy(&p, &u, 4);
+        }
+        if (isinf(p)) continue;
+        float q0 = p * y127;
+        float r = fmaf(-q0, d127, p);
+        float q1 = fmaf(r, y127, q0);
+        if (q1 != p / d127) ++bad;
+    }
     printf("%ld %ld\n", n, bad);
     return 0;
 }
