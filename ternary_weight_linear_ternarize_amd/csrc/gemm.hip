@@ -244,6 +244,220 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (M <= 16), weights streamed from HBM.
+//
+// The activation block (M x Kp int8) is copied into LDS once.  Each wave owns
+// 16 weight rows (one 16x16 MFMA tile; token rows M..15 are fed as zeros).
+// The weights are read the way the GEMV reads them -- every load instruction
+// covers LPR lanes x 16 bytes of one row, contiguous -- because the MFMA
+// operand layout (16 rows x 64 bytes per instruction) measured ~50 % slower
+// from HBM.  Each step of STEP weights per row goes registers -> a
+// wave-private LDS patch -> MFMA operands: lane (g, li) takes row li, words
+// 4g .. 4g+3 of each 256-weight block (k-step s uses word 4g + s and the
+// activation bytes at 64g + 16s of the block).  D steps of loads are in
+// flight while a step is computed.  NB = 2 runs the FFN's gate and up
+// weights together.
+template <int NB, int LPR, int WPB, int D, int EPI>
+__global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ rowsum, int M, int64_t Kp, const uint32_t* __restrict__ W0,
+    const float* __restrict__ s0, const uint32_t* __restrict__ W1, const float* __restrict__ s1,
+    int64_t N, float* __restrict__ Y, int32_t* __restrict__ acc_out,
+    float* __restrict__ gh_parts) {
+  constexpr int STEP = LPR * 64;                 // weights per row per step (16 B per lane)
+  constexpr int RPI = 64 / LPR;                  // rows per load instruction
+  constexpr int NI = 16 / RPI;                   // load instructions per matrix per step
+  constexpr int BP = STEP / 4 + 16;              // bytes per staged weight row (+ pad)
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  __shared__ float red[WPB][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t pitch = Kp + 16;                 // staged activation row
+  int8_t* lds_x = lds;
+  int8_t* lds_w = lds + ((M * pitch + 15) / 16) * 16 + (int64_t)wave * NB * 16 * BP;
+  const int64_t wpr = Kp / 16;
+  const int C = (int)(Kp / 64);                  // 16-byte pieces per row
+  const int nsteps = (int)((Kp + STEP - 1) / STEP);
+  const int64_t nbase = (int64_t)blockIdx.x * (16 * WPB) + 16 * wave;  // first row of the tile
+  const int lr = lane / LPR, lc = lane % LPR;    // load role: row-in-instruction, piece
+
+  // D steps of weights in flight, in registers
+  uint4 st[D][NB][NI];
+  auto load_step = [&](int sidx, uint4 (&dst)[NB][NI]) {
+#pragma unroll
+    for (int mat = 0; mat < NB; ++mat) {
+      const uint32_t* W = mat == 0 ? W0 : W1;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        int64_t n = nbase + RPI * i + lr;
+        n = n < N ? n : N - 1;
+        const int c = sidx * LPR + lc;
+        dst[mat][i] = c < C ? load_stream_u4(reinterpret_cast<const uint4*>(W + n * wpr) + c)
+                            : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+      }
+    }
+  };
+  auto stage_step = [&](const uint4 (&src)[NB][NI]) {
+#pragma unroll
+    for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<uint4*>(lds_w + (mat * 16 + RPI * i + lr) * BP + 16 * lc) = src[mat][i];
+  };
+  auto wave_sync = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nsteps) load_step(d, st[d]);
+  // activations -> LDS
+  const int64_t pieces = Kp / 16;
+  for (int64_t u = tid; u < (int64_t)M * pieces; u += 64 * WPB) {
+    const int64_t m = u / pieces, c = u - m * pieces;
+    *reinterpret_cast<uint4*>(lds_x + m * pitch + 16 * c) =
+        *reinterpret_cast<const uint4*>(Xq + m * Kp + 16 * c);
+  }
+  __syncthreads();
+
+  v4i acc[NB][2];
+#pragma unroll
+  for (int mat = 0; mat < NB; ++mat) acc[mat][0] = acc[mat][1] = v4i{0, 0, 0, 0};
+  const bool arow = li < M;
+  const int8_t* xrow = lds_x + (arow ? li : 0) * pitch + 64 * g;
+
+  for (int sbase = 0; sbase < nsteps; sbase += D) {
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int sidx = sbase + d;
+    if (sidx >= nsteps) break;
+    stage_step(st[d]);
+    wave_sync();
+    if (sidx + D < nsteps) load_step(sidx + D, st[d]);
+    const int64_t k0 = (int64_t)sidx * STEP;
+#pragma unroll
+    for (int b = 0; b < STEP / 256; ++b) {
+      if (k0 + 256 * b < Kp) {
+        uint4 bw[NB];
+#pragma unroll
+        for (int mat = 0; mat < NB; ++mat)
+          bw[mat] = *reinterpret_cast<const uint4*>(lds_w + (mat * 16 + li) * BP + 64 * b + 16 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int64_t ka = k0 + 256 * b + 64 * g + 16 * s;  // this lane's activation bytes
+          v4i a = v4i{0, 0, 0, 0};
+          if (arow && ka < Kp) a = *reinterpret_cast<const v4i*>(xrow + k0 + 256 * b + 16 * s);
+#pragma unroll
+          for (int mat = 0; mat < NB; ++mat) {
+            const uint32_t wd = s == 0 ? bw[mat].x : s == 1 ? bw[mat].y : s == 2 ? bw[mat].z : bw[mat].w;
+            acc[mat][s & 1] =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_operand(wd), acc[mat][s & 1], 0, 0, 0);
+          }
+        }
+      }
+    }
+    wave_sync();
+  }
+  }
+
+  // result lane l, register r: token 4g + r, weight row nbase + li
+  const int64_t n = nbase + li;
+  if constexpr (EPI == MF_STORE) {
+    const float sw = s0[0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      if (m < M && n < N) {
+        const int a = acc[0][0][r] + acc[0][1][r] - rowsum[m];
+        Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
+        if (acc_out) acc_out[(int64_t)m * N + n] = a;
+      }
+    }
+  } else {
+    const float sg = s0[0], su = s1[0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      float hm = 0.0f;
+      if (m < M && n < N) {
+        const int32_t rsm = rowsum[m];
+        const float xs = x_scale[m];
+        const float gv = dequant_fast(acc[0][0][r] + acc[0][1][r] - rsm, __fmul_rn(sg, xs));
+        const float uv = dequant_fast(acc[1][0][r] + acc[1][1][r] - rsm, __fmul_rn(su, xs));
+        const float t = gv > 0.0f ? gv : 0.0f;
+        const float h = __fmul_rn(__fmul_rn(t, t), uv);
+        Y[(int64_t)m * N + n] = h;
+        hm = fabsf(h);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) hm = fmaxf(hm, __shfl_xor(hm, o));
+      if (li == 0) red[wave][m] = hm;
+    }
+    __syncthreads();
+    if (tid < 16 && tid < M) {
+      float v = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < WPB; ++w) v = fmaxf(v, red[w][tid]);
+      gh_parts[(int64_t)blockIdx.x * M + tid] = v;
+    }
+  }
+}
+
+// Activation bytes the streaming kernel may stage in LDS.
+constexpr int64_t kStreamLds = 144 * 1024;
+
+// the activation block plus one wave's weight patches (two matrices)
+static bool stream_ok(int64_t M, int64_t Kp) {
+  return M <= 16 && M * (Kp + 16) + 2 * 16 * (32 * 16 + 16) <= kStreamLds;
+}
+
+// Dynamic LDS above 64 KiB has to be allowed per kernel once.
+template <typename Kern>
+static void allow_lds(Kern k) {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLds);
+}
+
+template <int NB, int WPB, int EPI>
+static hipError_t stream_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                            int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
+                            const float* s1, int64_t N, float* Y, int32_t* acc_out,
+                            float* gh_parts, int* nparts, hipStream_t s) {
+  constexpr int LPR = 32;
+  constexpr int BP = LPR * 16 + 16;
+  const size_t lds = (size_t)((M * (Kp + 16) + 15) / 16 * 16) + (size_t)WPB * NB * 16 * BP;
+  const unsigned blocks = (unsigned)((N + 16 * WPB - 1) / (16 * WPB));
+  if (nparts) *nparts = (int)blocks;
+  constexpr int D = 1;  // steps of weights in flight (2 and 4 measured slower: VGPR pressure)
+  static bool once = (allow_lds(mfma_stream_kernel<NB, LPR, WPB, D, EPI>), true);
+  (void)once;
+  hipLaunchKernelGGL((mfma_stream_kernel<NB, LPR, WPB, D, EPI>), dim3(blocks), dim3(64 * WPB), lds, s,
+                     Xq, xs, rs, (int)M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts);
+  return hipGetLastError();
+}
+
+// Waves per block: as many as keep about 200 blocks (most of the 256 CUs
+// busy) -- more waves per block share one staged copy of the activations.
+template <int NB, int EPI>
+static hipError_t stream_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                                int64_t Kp, const uint32_t* W0, const float* s0,
+                                const uint32_t* W1, const float* s1, int64_t N, float* Y,
+                                int32_t* acc_out, float* gh_parts, int* nparts, hipStream_t s) {
+  auto fits = [&](int wpb) {
+    return M * (Kp + 16) + (int64_t)wpb * NB * 16 * (32 * 16 + 16) <= kStreamLds;
+  };
+  if (N >= 200 * 128 && fits(8))
+    return stream_go<NB, 8, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
+  if (N >= 200 * 64 && fits(4))
+    return stream_go<NB, 4, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
+  if (N >= 200 * 32 && fits(2))
+    return stream_go<NB, 2, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
+  return stream_go<NB, 1, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
+}
+
 template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
 static hipError_t mfma_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                               int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
@@ -264,6 +478,9 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
   if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
+  if (stream_ok(M, Kp))
+    return stream_launch<1, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
+                                      nullptr, nullptr, s);
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
@@ -278,9 +495,9 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
 }
 
 int64_t mfma_gateup_parts(int64_t M, int64_t N) {
-  // the narrowest block used by launch_mfma_gateup is 64 columns
+  // the narrowest block used by launch_mfma_gateup covers 16 columns
   (void)M;
-  return (N + 63) / 64;
+  return (N + 15) / 16;
 }
 
 hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
@@ -288,6 +505,9 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
                               hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
+  if (stream_ok(M, Kp))
+    return stream_launch<2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr, gh_parts,
+                                       nparts, s);
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                               gh_parts, nparts, s);
