@@ -528,12 +528,17 @@ namespace bl {
 hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s) {
-  constexpr int TM = 4, TN = 2, WM = 1, WN = 4, KCH = 256;
-  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+  constexpr int TM = 4, TN = 2, WM = 1, WN = 4;
+  using G = TiledGemm<TM, TN, WM, WN>;
+  static bool once = ((void)hipFuncSetAttribute(
+                          reinterpret_cast<const void*>(tiled_gemm_kernel<TM, TN, WM, WN>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS),
+                      true);
+  (void)once;
   const int64_t Kp = (K + 63) / 64 * 64;
-  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((mfma32_gemm_kernel<TM, TN, WM, WN, KCH>), dim3((unsigned)(nbm * nbn)), dim3(256),
-                     0, s, Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, (int)nbm, (int)nbn);
+  const int64_t nbm = (M + G::BM - 1) / G::BM, nbn = (N + G::BN - 1) / G::BN;
+  hipLaunchKernelGGL((tiled_gemm_kernel<TM, TN, WM, WN>), dim3((unsigned)(nbm * nbn)), dim3(256),
+                     G::LDS, s, Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, (int)nbm);
   return hipGetLastError();
 }
 

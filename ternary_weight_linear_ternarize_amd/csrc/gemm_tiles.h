@@ -1,10 +1,20 @@
-// Tiled ternary x int8 GEMM kernel template (v_mfma_i32_32x32x32_i8).
+// Tiled ternary x int8 GEMM kernel (v_mfma_i32_32x32x32_i8) for M > 64.
 #pragma once
 
 #include "bl_device.h"
 
 namespace bl {
 
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+
+// Raw buffer resource over [base, base + nbytes): loads past nbytes return 0.
+__device__ __forceinline__ buf_rsrc make_buf_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+
+// The four shifted-code byte vectors of one packed word (weights 16j + 4s + b
+// of the word sit in byte b of vector s).
 __device__ __forceinline__ v4i unpack_operand32(uint32_t w) {
   v4i r;
   r[0] = (int)(w & 0x03030303u);
@@ -14,106 +24,130 @@ __device__ __forceinline__ v4i unpack_operand32(uint32_t w) {
   return r;
 }
 
-__device__ __forceinline__ uint32_t pick32(const uint4& v, int s) {
-  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+__device__ __forceinline__ uint32_t pick32(const u32x4& v, int s) {
+  return s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
+}
+
+// ((float)a * s) / 127 with one rounding per operation, as dequant(), computed
+// as RN32(RN64(p * RN64(1/127))) with p = RN32(a * s).  This is exact: p has
+// at most 24 significant bits, so p / 127 differs from every binary32 rounding
+// midpoint by at least 2^-25 / 127 of its magnitude (127 is odd, a midpoint
+// has 25 bits), far more than the 2^-52 relative error of the binary64
+// product.  Holds for subnormal quotients too (binary64 keeps them normal).
+__device__ __forceinline__ float dequant_f64(int a, float s) {
+  const float p = __fmul_rn((float)a, s);
+  return (float)((double)p * (1.0 / 127.0));
 }
 
 // ---------------------------------------------------------------------------
-// Prefill GEMM on v_mfma_i32_32x32x32_i8.
+// Block tile BM x BN = (32 TM WAVES_M) x (32 TN WAVES_N), 4 waves, wave tile
+// (32 TM) x (32 TN).  K advances in chunks of 256 (10 for K = 2560):
 //
-// Block tile BM x BN, 4 waves as WAVES_M x WAVES_N, wave tile (32 TM) x (32 TN).
-// K advances in chunks of KCH: the activation chunk (BM x KCH int8) is staged
-// through LDS (double buffered, rows padded by 16 bytes so the 32 rows a wave
-// reads at one offset spread over the banks); the packed weight chunk goes
-// straight to registers (KCH/32 words per lane per 32-row tile).  Loads of
-// chunk c+1 are issued before chunk c is computed.
+//  * activations: BM x 256 int8 per chunk go HBM/L2 -> LDS directly
+//    (buffer_load ... lds, 64 lanes x 16 bytes per load = 4 rows x 256 bytes),
+//    double buffered.  Each load writes 1 KB of LDS in lane order; the lane
+//    that lands in 16-byte slot t of row r fetches logical piece t ^ (r % 16),
+//    so a wave reading piece p of 32 consecutive rows hits 16 distinct bank
+//    groups (conflict-free ds_read_b128) while every load still covers whole
+//    256-byte row segments of global memory.
+//  * packed weights go straight to registers (buffer loads, double buffered
+//    across chunks): lane (li, g) of 32-row tile tn holds words 8g .. 8g+7 of
+//    the chunk for weight row 32 tn + li.
 //
-// Result layout of one 32x32 tile (lane l, g = l / 32, register r):
-// token row 8 (r / 4) + 4 g + (r % 4), weight row l % 32.
+// MFMA operands: in k-step s of a chunk, lane (li, g) supplies activation
+// bytes 16 (8g + s) .. +15 of token row li and the four code vectors of
+// packed word 8g + s of weight row li; both cover the same 16 k positions, and
+// the MFMA sums over all k of the step whatever their order among lanes.
 //
-// Blocks are numbered so that block b runs on XCD b % 8; the M tiles are
-// spread over XCDs (bm varies fastest within a round of 8) so the blocks one
-// XCD runs share activation rows in that XCD's L2.
+// The accumulators start at -rowsum (per token row), so they end as
+// sum q (t + 1) - sum q = sum q t.  Result layout of one 32x32 tile (lane l,
+// g = l / 32, register r): token row 8 (r / 4) + 4 g + (r % 4), weight row
+// l % 32; the epilogue dequantises in registers and stores each register as
+// two full 128-byte row segments (non-temporal: Y is not read back here).
+//
+// Out-of-range rows and the K tail read as zero through the buffer
+// resources' bounds, so the main loop has no per-lane range checks.  Block b
+// runs on XCD b % 8; bm varies fastest so the blocks one XCD runs share
+// activation rows in its L2.
+template <int TM, int TN, int WAVES_M, int WAVES_N>
+struct TiledGemm {
+  static constexpr int KCH = 256;
+  static constexpr int BM = 32 * TM * WAVES_M, BN = 32 * TN * WAVES_N;
+  static constexpr int ABYTES = BM * KCH;  // one LDS stage of activations
+  static constexpr int NLD = BM / 16;      // direct loads per wave per chunk
+  static constexpr int LDS = 2 * ABYTES + 8 * BM;
+};
 
-// KCH: K per chunk (a multiple of 64); lane group g holds words
-// (KCH/32) g .. (KCH/32) g + KCH/32 - 1 of each chunk row, and k-step s
-// (0 <= s < KCH/32) uses word (KCH/32) g + s with the activation bytes at
-// 16 ((KCH/32) g + s).
-template <int TM, int TN, int WAVES_M, int WAVES_N, int KCH>
-__global__ __launch_bounds__(256, 2) void mfma32_gemm_kernel(
+template <int TM, int TN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp, const uint32_t* __restrict__ W,
     const float* __restrict__ w_scale, int64_t N, float* __restrict__ Y,
-    int32_t* __restrict__ acc_out, int nbm, int nbn) {
+    int32_t* __restrict__ acc_out, int nbm) {
+  using G = TiledGemm<TM, TN, WAVES_M, WAVES_N>;
+  constexpr int KCH = G::KCH, BM = G::BM, BN = G::BN, ABYTES = G::ABYTES, NLD = G::NLD;
+  constexpr int WPL = KCH / 32;  // k-steps per chunk
+  constexpr uint32_t kOOB = 0x80000000u;  // an offset past every resource
   static_assert(WAVES_M * WAVES_N == 4, "4 waves per block");
-  constexpr int BM = 32 * TM * WAVES_M;
-  constexpr int BN = 32 * TN * WAVES_N;
-  constexpr int PITCH = KCH + 16;             // padded row: spreads a column over all banks
-  constexpr int CPR = KCH / 16;               // 16-byte pieces per row per chunk
-  constexpr int A_U4 = BM * CPR / 256;        // uint4 per thread per chunk
-  constexpr int WPL = KCH / 32;               // words per lane per chunk = k-steps
-  constexpr int BU4 = WPL / 4;                // uint4 per lane per 32-row tile
-  static_assert(A_U4 >= 1 && WPL % 4 == 0, "tile shape");
-  __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * PITCH];
-  __shared__ float lds_sc[BM];    // g_w * g_x per token row of the tile
-  __shared__ int32_t lds_rs[BM];  // row sums of the codes
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  float* lds_sc = reinterpret_cast<float*>(lds + 2 * ABYTES);
+  int32_t* lds_rs = reinterpret_cast<int32_t*>(lds + 2 * ABYTES + 4 * BM);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int g = lane >> 5, li = lane & 31;
-  // block -> tile: bm fastest, so the blocks of one XCD (b % 8) share A rows
   const int bm = blockIdx.x % nbm, bn = blockIdx.x / nbm;
   const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
   const int64_t wpr = Kp / 16;
   const int nchunks = (int)((Kp + KCH - 1) / KCH);
+  const int mrows = (int)(M - m0 < BM ? M - m0 : BM);
+  const int nrows = (int)(N - n0 < BN ? N - n0 : BN);
+  const buf_rsrc ra = make_buf_rsrc(Xq + m0 * Kp, (uint32_t)(mrows * Kp));
+  const buf_rsrc rb = make_buf_rsrc(W + n0 * wpr, (uint32_t)(nrows * wpr * 4));
 
-  uint4 a_reg[A_U4];
-  auto load_a = [&](int64_t kc) {
+  // activation loads: load j of this wave fills rows 4 (wave NLD + j) + lane / 16
+  uint32_t a_off[NLD];
+  int a_pl[NLD];
 #pragma unroll
-    for (int i = 0; i < A_U4; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / CPR, c16 = u % CPR;
-      const int64_t m = m0 + row, k = kc + 16 * c16;
-      if (m < M && k < Kp)
-        a_reg[i] = *reinterpret_cast<const uint4*>(Xq + m * Kp + k);
-      else
-        a_reg[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = 0; j < NLD; ++j) {
+    const int row = 4 * (wave * NLD + j) + (lane >> 4);
+    a_pl[j] = (lane & 15) ^ (row & 15);
+    a_off[j] = (uint32_t)(row * Kp + 16 * a_pl[j]);
+  }
+  auto issue_a = [&](int c, int buf) {
+    const int64_t kc = (int64_t)c * KCH;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const uint32_t off = (kc + 16 * a_pl[j] < Kp) ? a_off[j] + (uint32_t)kc : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds + buf * ABYTES + (wave * NLD + j) * 1024, 16,
+                                               off, 0, 0, 0);
     }
   };
-  auto store_a = [&](int buf) {
+  uint32_t b_off[TN];
 #pragma unroll
-    for (int i = 0; i < A_U4; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / CPR, c16 = u % CPR;
-      *reinterpret_cast<uint4*>(&lds_a[buf][row * PITCH + 16 * c16]) = a_reg[i];
-    }
-  };
-  uint4 b_reg[TN][BU4];
-  auto load_b = [&](int64_t kc) {
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      const int64_t n = n0 + 32 * (wn * TN + tn) + li;
-#pragma unroll
-      for (int q = 0; q < BU4; ++q) {
-        const int64_t word = kc / 16 + WPL * g + 4 * q;
-        if (n < N && word < wpr)
-          b_reg[tn][q] = *reinterpret_cast<const uint4*>(W + n * wpr + word);
-        else
-          b_reg[tn][q] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-
-  v16i acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tn = 0; tn < TN; ++tn)
+    b_off[tn] = (uint32_t)(((32 * (wn * TN + tn) + li) * wpr + 8 * g) * 4);
+  auto issue_b = [&](int c, u32x4 (&dst)[TN][2]) {
+    const int64_t w0 = (int64_t)c * (KCH / 16);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0;
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t off =
+            (w0 + 8 * g + 4 * q < wpr) ? b_off[tn] + (uint32_t)((w0 + 4 * q) * 4) : kOOB;
+        dst[tn][q] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+      }
+  };
+  // LDS byte offset of the activation operand of k-step s (tile tm adds 32 tm rows)
+  uint32_t a_rd[WPL];
+#pragma unroll
+  for (int s = 0; s < WPL; ++s)
+    a_rd[s] = (uint32_t)((32 * wm * TM + li) * KCH + 16 * ((8 * g + s) ^ (li & 15)));
 
-  load_a(0);
-  load_b(0);
+  u32x4 bA[TN][2], bB[TN][2];
+  issue_a(0, 0);
+  issue_b(0, bA);
   {
     const float sw = w_scale[0];
     for (int i = tid; i < BM; i += 256) {
@@ -122,85 +156,79 @@ __global__ __launch_bounds__(256, 2) void mfma32_gemm_kernel(
       lds_rs[i] = m < M ? rowsum[m] : 0;
     }
   }
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    store_a(buf);
-    uint4 b_cur[TN][BU4];
+  __syncthreads();
+  v16i acc[TM][TN];
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
+  for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-      for (int q = 0; q < BU4; ++q) b_cur[tn][q] = b_reg[tn][q];
-    __syncthreads();
-    if (c + 1 < nchunks) {
-      load_a((int64_t)(c + 1) * KCH);
-      load_b((int64_t)(c + 1) * KCH);
+    for (int r = 0; r < 16; ++r) {
+      const int v = -lds_rs[32 * (wm * TM + tm) + 8 * (r >> 2) + 4 * g + (r & 3)];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[tm][tn][r] = v;
     }
-    const int8_t* la = &lds_a[buf][0];
+
+  auto compute = [&](int buf, const u32x4 (&b)[TN][2]) {
+    const int8_t* base = lds + buf * ABYTES;
+    v4i a[2][TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      a[0][tm] = *reinterpret_cast<const v4i*>(base + a_rd[0] + tm * 32 * KCH);
 #pragma unroll
     for (int s = 0; s < WPL; ++s) {
-      v4i a[TM];
+      if (s + 1 < WPL) {
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int row = 32 * (wm * TM + tm) + li;
-        a[tm] = *reinterpret_cast<const v4i*>(la + row * PITCH + 16 * (WPL * g + s));
+        for (int tm = 0; tm < TM; ++tm)
+          a[(s + 1) & 1][tm] = *reinterpret_cast<const v4i*>(base + a_rd[s + 1] + tm * 32 * KCH);
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const v4i b = unpack_operand32(pick32(b_cur[tn][s >> 2], s & 3));
+        const v4i bv = unpack_operand32(pick32(b[tn][s >> 2], s & 3));
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
-          acc[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[tm], b, acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s & 1][tm], bv, acc[tm][tn], 0, 0, 0);
       }
     }
+  };
+  // Chunk c: wait for its loads (issued one chunk earlier), then start chunk
+  // c + 1's loads into the other buffers and compute.  The barrier also
+  // guarantees every wave has finished reading the buffer about to be refilled.
+  auto step = [&](int c, int buf, const u32x4 (&cur)[TN][2], u32x4 (&nxt)[TN][2]) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c + 1 < nchunks) {
+      issue_a(c + 1, buf ^ 1);
+      issue_b(c + 1, nxt);
+    }
+    compute(buf, cur);
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, 0, bA, bB);
+    if (c + 1 < nchunks) step(c + 1, 1, bB, bA);
   }
 
-  // Epilogue: dequantise one 32x32 tile at a time into a wave-private LDS
-  // patch, then write whole 16-byte runs of Y rows (non-temporal: Y is
-  // written once and not read back here).
-  constexpr int OP = 36;  // floats per staged row (32 + 4 pad)
-  static_assert(4 * 32 * OP * 4 <= 2 * BM * PITCH, "staging fits in the A buffers");
-  __syncthreads();
-  float* st = reinterpret_cast<float*>(&lds_a[0][0]) + wave * 32 * OP;
-  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15) == 0;
+  // Epilogue straight from the accumulators.
+  const bool interior = mrows == BM && nrows == BN && !acc_out;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
+    for (int r = 0; r < 16; ++r) {
+      const int ml = 32 * (wm * TM + tm) + 8 * (r >> 2) + 4 * g + (r & 3);
+      const float sc = lds_sc[ml];
+      float* yrow = Y + (m0 + ml) * N + n0 + 32 * wn * TN + li;
+      if (interior) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rl = 8 * (r >> 2) + 4 * g + (r & 3);
-        const int ml = 32 * (wm * TM + tm) + rl;
-        const int a = acc[tm][tn][r] - lds_rs[ml];
-        st[rl * OP + li] = dequant_fast(a, lds_sc[ml]);
-        if (acc_out) {
-          const int64_t m = m0 + ml, n = n0 + 32 * (wn * TN + tn) + li;
-          if (m < M && n < N) acc_out[m * N + n] = a;
+        for (int tn = 0; tn < TN; ++tn)
+          __builtin_nontemporal_store(dequant_f64(acc[tm][tn][r], sc), yrow + 32 * tn);
+      } else if (ml < mrows) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int nl = 32 * (wn * TN + tn) + li;
+          if (nl < nrows) {
+            __builtin_nontemporal_store(dequant_f64(acc[tm][tn][r], sc), yrow + 32 * tn);
+            if (acc_out) acc_out[(m0 + ml) * N + n0 + nl] = acc[tm][tn][r];
+          }
         }
       }
-      // the patch is private to this wave: a wave-level barrier orders it
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int idx = lane + 64 * j;  // float4 index in the 32 x 32 patch
-        const int rl = idx >> 3, c4 = idx & 7;
-        const int64_t m = m0 + 32 * (wm * TM + tm) + rl;
-        const int64_t n = n0 + 32 * (wn * TN + tn) + 4 * c4;
-        if (m >= M) continue;
-        const float* src = st + rl * OP + 4 * c4;
-        if (vec && n + 3 < N) {
-          f32x4 v = {src[0], src[1], src[2], src[3]};
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(Y + m * N + n));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) Y[m * N + n + e] = src[e];
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
