@@ -3,7 +3,10 @@
  * q1 must equal the IEEE quotient RN(a/d) (Markstein's correction).  Pairs
  * are drawn over the kernels' operating range (d = scale + 1e-5 >= 1e-5,
  * below 2^100; |a/d| <= 127), half of them with a/d next to k + 1/2 where
- * the int8 code could flip.  Prints "<pairs> <quotient mismatches>". */
+ * the int8 code could flip.  Also checks the binary64 route of the GEMM
+ * epilogue, RN32(RN64(p * RN64(1/127))) == RN32(p / 127), on random binary32
+ * p over the whole finite range (subnormals included) and on every mantissa
+ * of three binades.  Prints "<pairs> <quotient mismatches>". */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -60,6 +63,21 @@ int main(int argc, char **argv) {
         float q1 = fmaf(r, y127, q0);
         if (q1 != p / d127) ++bad;
     }
+    /* binary64 product route for the division by 127 */
+    const double r127 = 1.0 / 127.0;
+    for (long i = 0; i < n; ++i) {
+        uint32_t u = (uint32_t)next();
+        float p;
+        memcpy(&p, &u, 4);
+        if (isnan(p) || isinf(p)) continue;
+        if ((float)((double)p * r127) != p / 127.0f) ++bad;
+    }
+    const int exps[3] = {-140, 0, 100}; /* subnormal quotients, ordinary, large */
+    for (int e = 0; e < 3; ++e)
+        for (uint32_t m = 0; m < (1u << 23); ++m) {
+            float p = ldexpf(1.0f + (float)m / 8388608.0f, exps[e]);
+            if ((float)((double)p * r127) != p / 127.0f) ++bad;
+        }
     printf("%ld %ld\n", n, bad);
     return 0;
 }

@@ -1,6 +1,8 @@
-"""Host check of the reciprocal-and-correction division used by the int8
-activation quantisers (see bl_device.h, quant_code_fast): it must give the
-IEEE-rounded quotient, hence the same int8 codes as a plain division."""
+"""Host check of the divisions the kernels replace: the reciprocal-and-
+correction division of the int8 activation quantisers (bl_device.h,
+quant_code_fast) and the binary64 product used for the division by 127 in
+the GEMM epilogue (gemm_tiles.h, dequant_f64).  Both must give the IEEE-rounded
+binary32 quotient, hence the same codes and outputs as a plain division."""
 import os
 import shutil
 import subprocess
