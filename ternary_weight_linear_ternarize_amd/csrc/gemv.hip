@@ -11,8 +11,10 @@
 // lane l taking the 64-weight chunks l, l+64, ... (16 bytes of 2-bit codes:
 // one dwordx4 load per row and chunk), so each row is one contiguous stream
 // and a wave-wide load covers up to 1 KiB.  All weight loads of a wave are
-// issued before anything waits on them.  The activation chunk of a lane is
-// the same for every row and stays in registers.  The R per-lane partial sums
+// issued before anything waits on them.  The activation codes are staged
+// once per block in LDS and read chunk by chunk (64 bytes per lane, the same
+// for every row), which keeps the register count low enough for every wave of
+// a large layer to be resident at once.  The R per-lane partial sums
 // are reduced across the wave with a transposing butterfly, and the epilogue
 // dequantises: y = ((float)acc * (g_w * g_x)) / 127.
 //
@@ -118,9 +120,48 @@ __device__ __forceinline__ void gemv_load_w(const GemvArgs& a, int64_t rb, int l
   }
 }
 
+// LDS byte offset of 16-byte piece p of the activation codes.  The four
+// pieces of 64-weight chunk c are rotated by (c / 2) % 4, so the eight lanes
+// of a ds_read_b128 phase (consecutive chunks, same piece) hit eight
+// different 16-byte bank groups.
+__device__ __forceinline__ int xslot(int p) {
+  const int c = p >> 2;
+  return 16 * (4 * c + ((p & 3) ^ ((c >> 1) & 3)));
+}
+
+// Partial dot products of this lane's chunks (lane, lane + 64, ...) with the
+// codes in LDS.
 template <int KC, int R>
-__device__ __forceinline__ void gemv_dots(const uint4 (&w)[R][KC], const int (&x)[KC][16],
-                                          int (&part)[R]) {
+__device__ __forceinline__ void gemv_dots(const uint4 (&w)[R][KC], const int8_t* xq_lds, int lane,
+                                          int C, int (&part)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) part[r] = 0;
+#pragma unroll
+  for (int i = 0; i < KC; ++i) {
+    const int c = lane + 64 * i;
+    int4 xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xv[q] = c < C ? *reinterpret_cast<const int4*>(xq_lds + xslot(4 * c + q))
+                    : make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      Dot16 d;
+      d.add(w[r][i].x, xv[0].x, xv[0].y, xv[0].z, xv[0].w);
+      d.add(w[r][i].y, xv[1].x, xv[1].y, xv[1].z, xv[1].w);
+      d.add(w[r][i].z, xv[2].x, xv[2].y, xv[2].z, xv[2].w);
+      d.add(w[r][i].w, xv[3].x, xv[3].y, xv[3].z, xv[3].w);
+      part[r] += d.total();
+    }
+    // one chunk of codes live at a time (keeps the register count down)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The same with the codes of this lane's chunks in registers.
+template <int KC, int R>
+__device__ __forceinline__ void gemv_dots_regs(const uint4 (&w)[R][KC], const int (&x)[KC][16],
+                                               int (&part)[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     Dot16 d;
@@ -178,7 +219,7 @@ template <int KC, int R, int EPI, int XSRC>
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;  // output rows per wave
   constexpr bool FUSED = XSRC != XS_INT8;
-  __shared__ __attribute__((aligned(16))) int8_t xq_lds[FUSED ? 4096 * KC : 16];
+  __shared__ __attribute__((aligned(16))) int8_t xq_lds[4096 * KC];
   __shared__ float redf[4];
   __shared__ int redi[4];
 
@@ -187,6 +228,50 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   const int wpr = (int)(a.Kp >> 4);
   const int64_t rb = (int64_t)blockIdx.x * 4 + wave;  // this wave's row block
 
+  // Activation loads are issued before the weight loads: vmcnt counts in
+  // order, so waiting for the activations then leaves the weights in flight
+  // and the staging/quantisation below overlaps the weight stream.
+  constexpr int NWT = 4 * KC;  // fused: words per thread (Kp <= 4096 * KC)
+  int4 xi[KC];
+  float xv[NWT][4];
+  float g = 0.0f;
+  if constexpr (!FUSED) {
+    const int4* xg = reinterpret_cast<const int4*>(a.x);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int p = tid + 256 * j;
+      xi[j] = p < 4 * C ? xg[p] : make_int4(0, 0, 0, 0);
+    }
+  } else {
+    const int K = (int)a.K, nw = (int)(a.Kp >> 2);
+    if constexpr (XSRC == XS_PARTS) {
+      for (int p = tid; p < a.nparts; p += 256) g = fmaxf(g, a.gparts[p]);
+    }
+    const bool vec = (reinterpret_cast<uintptr_t>(a.x) & (XSRC == XS_BF16 ? 7 : 15)) == 0;
+#pragma unroll
+    for (int j = 0; j < NWT; ++j) {
+      const int wd = tid + 256 * j;
+      if (vec && 4 * wd + 3 < K) {
+        if constexpr (XSRC == XS_BF16) {
+          const uint2 u = reinterpret_cast<const uint2*>(a.x)[wd];
+          xv[j][0] = __uint_as_float(u.x << 16);
+          xv[j][1] = __uint_as_float(u.x & 0xffff0000u);
+          xv[j][2] = __uint_as_float(u.y << 16);
+          xv[j][3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 f = reinterpret_cast<const float4*>(a.x)[wd];
+          xv[j][0] = f.x; xv[j][1] = f.y; xv[j][2] = f.z; xv[j][3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int k = 4 * wd + b;
+          xv[j][b] = (wd < nw && k < K) ? load_act<XSRC == XS_BF16>(a.x, k) : 0.0f;
+        }
+      }
+    }
+  }
+
   uint4 w[R][KC];
   gemv_load_w<KC, R, EPI>(a, rb, lane, C, wpr, w);
 
@@ -194,48 +279,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   const float sw1 = (EPI == EPI_GATEUP) ? a.s1[0] : 0.0f;
   float gx = 0.0f;
   int rsum = 0;
-  int x[KC][16];
   if constexpr (!FUSED) {
     gx = a.x_scale[0];
     rsum = a.rowsum[0];
-    const int8_t* xq = reinterpret_cast<const int8_t*>(a.x);
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = lane + 64 * i;
-      const int cc = c < C ? c : C - 1;
-      const int4* p = reinterpret_cast<const int4*>(xq + 64 * cc);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int4 v = p[q];
-        if (c >= C) v = make_int4(0, 0, 0, 0);
-        x[i][4 * q + 0] = v.x; x[i][4 * q + 1] = v.y; x[i][4 * q + 2] = v.z; x[i][4 * q + 3] = v.w;
-      }
+    for (int j = 0; j < KC; ++j) {
+      const int p = tid + 256 * j;
+      if (p < 4 * C) *reinterpret_cast<int4*>(xq_lds + xslot(p)) = xi[j];
     }
+    __syncthreads();
   } else {
     // quantise the whole row into LDS (every block does the same, same bits)
-    const int K = (int)a.K, nw = (int)(a.Kp >> 2);
-    constexpr int NWT = 4 * KC;  // words per thread: Kp <= 4096 * KC
-    float xv[NWT][4];
-    float g = 0.0f;
-    if constexpr (XSRC == XS_PARTS) {
-      for (int p = tid; p < a.nparts; p += 256) g = fmaxf(g, a.gparts[p]);
-    }
+    const int nw = (int)(a.Kp >> 2);
+    if constexpr (XSRC != XS_PARTS) {
 #pragma unroll
-    for (int j = 0; j < NWT; ++j) {
-      const int wd = tid + 256 * j;
+      for (int j = 0; j < NWT; ++j)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int k = 4 * wd + b;
-        float v = 0.0f;
-        if (wd < nw && k < K) {
-          if constexpr (XSRC == XS_BF16)
-            v = load_act<true>(a.x, k);
-          else
-            v = load_act<false>(a.x, k);
-        }
-        xv[j][b] = v;
-        if constexpr (XSRC != XS_PARTS) g = fmaxf(g, fabsf(v));
-      }
+        for (int b = 0; b < 4; ++b) g = fmaxf(g, fabsf(xv[j][b]));
     }
     g = block_max4(g, redf);
     const QuantDiv qd = make_qdiv(g);
@@ -251,7 +311,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
           rs += c;
           pk |= ((uint32_t)(c & 0xff)) << (8 * b);
         }
-        reinterpret_cast<uint32_t*>(xq_lds)[wd] = pk;
+        *reinterpret_cast<uint32_t*>(xq_lds + xslot(wd >> 2) + 4 * (wd & 3)) = pk;
         if (blockIdx.x == 0 && a.xq_out) reinterpret_cast<uint32_t*>(a.xq_out)[wd] = pk;
       }
     }
@@ -261,22 +321,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
       if (a.xs_out) a.xs_out[0] = g;
       if (a.rs_out) a.rs_out[0] = rsum;
     }
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int c = lane + 64 * i;
-      const int cc = c < C ? c : C - 1;
-      const int4* p = reinterpret_cast<const int4*>(xq_lds + 64 * cc);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int4 v = p[q];
-        if (c >= C) v = make_int4(0, 0, 0, 0);
-        x[i][4 * q + 0] = v.x; x[i][4 * q + 1] = v.y; x[i][4 * q + 2] = v.z; x[i][4 * q + 3] = v.w;
-      }
-    }
   }
 
   int part[R];
-  gemv_dots<KC, R>(w, x, part);
+  gemv_dots<KC, R>(w, xq_lds, lane, C, part);
   float hmax = 0.0f;
   if (rb * RW < a.N) hmax = gemv_epilogue<R, EPI>(a, rb, part, rsum, gx, sw0, sw1);
 
@@ -332,7 +380,7 @@ __global__ __launch_bounds__(256) void gemv_long_kernel(const GemvArgs a) {
       }
     }
     int part[R];
-    gemv_dots<KC, R>(w, x, part);
+    gemv_dots_regs<KC, R>(w, x, part);
 #pragma unroll
     for (int r = 0; r < R; ++r) total[r] += part[r];
   }
