@@ -443,8 +443,8 @@ hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t
   a.xq_out = xq_out;
   a.xs_out = xs_out;
   a.rs_out = rs_out;
-  return bf16 ? gemv_dispatch<8, EPI_STORE, XS_BF16>(a, s)
-              : gemv_dispatch<8, EPI_STORE, XS_F32>(a, s);
+  return bf16 ? gemv_dispatch<4, EPI_STORE, XS_BF16>(a, s)
+              : gemv_dispatch<4, EPI_STORE, XS_F32>(a, s);
 }
 
 hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, int64_t K,
@@ -457,7 +457,7 @@ hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, in
   a.xq_out = xq_out;
   a.xs_out = xs_out;
   a.rs_out = rs_out;
-  return gemv_dispatch<8, EPI_STORE, XS_PARTS>(a, s);
+  return gemv_dispatch<4, EPI_STORE, XS_PARTS>(a, s);
 }
 
 constexpr int kGateupR = 4;  // weight rows per wave in the gate/up GEMV (half gate, half up)
