@@ -258,7 +258,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
 // activation bytes at 64g + 16s of the block).  D steps of loads are in
 // flight while a step is computed.  NB = 2 runs the FFN's gate and up
 // weights together.
-template <int NB, int LPR, int WPB, int D, int EPI>
+//
+// KS > 1 splits K: the KS waves of a tile take consecutive ranges of steps
+// and the partial accumulators of waves 1 .. KS-1 are added to wave 0's
+// through LDS before the epilogue (more waves in flight for layers with few
+// rows, e.g. the FFN's down projection).
+template <int NB, int LPR, int WPB, int D, int EPI, int KS>
 __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int M, int64_t Kp, const uint32_t* __restrict__ W0,
@@ -269,17 +274,24 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   constexpr int RPI = 64 / LPR;                  // rows per load instruction
   constexpr int NI = 16 / RPI;                   // load instructions per matrix per step
   constexpr int BP = STEP / 4 + 16;              // bytes per staged weight row (+ pad)
+  constexpr int TPB = WPB / KS;                  // 16-row tiles per block
+  static_assert(TPB * KS == WPB, "KS divides WPB");
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   __shared__ float red[WPB][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = wave / KS, kpart = wave % KS;
   const int g = lane >> 4, li = lane & 15;
   const int64_t pitch = Kp + 16;                 // staged activation row
   int8_t* lds_x = lds;
-  int8_t* lds_w = lds + ((M * pitch + 15) / 16) * 16 + (int64_t)wave * NB * 16 * BP;
+  const int64_t xbytes = ((M * pitch + 15) / 16) * 16;
+  int8_t* lds_w = lds + xbytes + (int64_t)wave * NB * 16 * BP;
+  v4i* lds_part = reinterpret_cast<v4i*>(lds + xbytes + (int64_t)WPB * NB * 16 * BP);
   const int64_t wpr = Kp / 16;
   const int C = (int)(Kp / 64);                  // 16-byte pieces per row
-  const int nsteps = (int)((Kp + STEP - 1) / STEP);
-  const int64_t nbase = (int64_t)blockIdx.x * (16 * WPB) + 16 * wave;  // first row of the tile
+  const int nsteps_all = (int)((Kp + STEP - 1) / STEP);
+  const int s_begin = kpart * nsteps_all / KS, s_end = (kpart + 1) * nsteps_all / KS;
+  const int nsteps = s_end - s_begin;            // this wave's steps
+  const int64_t nbase = (int64_t)blockIdx.x * (16 * TPB) + 16 * tile;  // first row of the tile
   const int lr = lane / LPR, lc = lane % LPR;    // load role: row-in-instruction, piece
 
   // D steps of weights in flight, in registers
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
       for (int i = 0; i < NI; ++i) {
         int64_t n = nbase + RPI * i + lr;
         n = n < N ? n : N - 1;
-        const int c = sidx * LPR + lc;
+        const int c = (s_begin + sidx) * LPR + lc;
         dst[mat][i] = c < C ? load_stream_u4(reinterpret_cast<const uint4*>(W + n * wpr) + c)
                             : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
       }
@@ -337,7 +349,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     stage_step(st[d]);
     wave_sync();
     if (sidx + D < nsteps) load_step(sidx + D, st[d]);
-    const int64_t k0 = (int64_t)sidx * STEP;
+    const int64_t k0 = (int64_t)(s_begin + sidx) * STEP;
 #pragma unroll
     for (int b = 0; b < STEP / 256; ++b) {
       if (k0 + 256 * b < Kp) {
@@ -363,6 +375,26 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   }
   }
 
+  // K split: fold the partial sums of waves 1 .. KS-1 into wave 0 of the tile
+#pragma unroll
+  for (int mat = 0; mat < NB; ++mat) acc[mat][0] += acc[mat][1];
+  if constexpr (KS > 1) {
+    if (kpart > 0) {
+#pragma unroll
+      for (int mat = 0; mat < NB; ++mat)
+        lds_part[((tile * (KS - 1) + kpart - 1) * NB + mat) * 64 + lane] = acc[mat][0];
+    }
+    __syncthreads();
+    if (kpart == 0) {
+#pragma unroll
+      for (int k = 1; k < KS; ++k)
+#pragma unroll
+        for (int mat = 0; mat < NB; ++mat)
+          acc[mat][0] += lds_part[((tile * (KS - 1) + k - 1) * NB + mat) * 64 + lane];
+    }
+  }
+  const bool owner = kpart == 0;
+
   // result lane l, register r: token 4g + r, weight row nbase + li
   const int64_t n = nbase + li;
   if constexpr (EPI == MF_STORE) {
@@ -370,8 +402,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
-      if (m < M && n < N) {
-        const int a = acc[0][0][r] + acc[0][1][r] - rowsum[m];
+      if (owner && m < M && n < N) {
+        const int a = acc[0][0][r] - rowsum[m];
         Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
@@ -382,11 +414,11 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
       float hm = 0.0f;
-      if (m < M && n < N) {
+      if (owner && m < M && n < N) {
         const int32_t rsm = rowsum[m];
         const float xs = x_scale[m];
-        const float gv = dequant_fast(acc[0][0][r] + acc[0][1][r] - rsm, __fmul_rn(sg, xs));
-        const float uv = dequant_fast(acc[1][0][r] + acc[1][1][r] - rsm, __fmul_rn(su, xs));
+        const float gv = dequant_fast(acc[0][0][r] - rsm, __fmul_rn(sg, xs));
+        const float uv = dequant_fast(acc[1][0][r] - rsm, __fmul_rn(su, xs));
         const float t = gv > 0.0f ? gv : 0.0f;
         const float h = __fmul_rn(__fmul_rn(t, t), uv);
         Y[(int64_t)m * N + n] = h;
@@ -421,41 +453,54 @@ static void allow_lds(Kern k) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLds);
 }
 
-template <int NB, int WPB, int EPI>
+constexpr int kStreamLpr = 32;
+constexpr int kStreamBp = kStreamLpr * 16 + 16;  // staged bytes per weight row and step
+
+static int64_t stream_lds_bytes(int64_t M, int64_t Kp, int nb, int wpb, int ks) {
+  return (M * (Kp + 16) + 15) / 16 * 16 + (int64_t)wpb * nb * 16 * kStreamBp +
+         (int64_t)(wpb / ks) * (ks - 1) * nb * 1024;
+}
+
+template <int NB, int WPB, int KS, int EPI>
 static hipError_t stream_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                             int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
                             const float* s1, int64_t N, float* Y, int32_t* acc_out,
                             float* gh_parts, int* nparts, hipStream_t s) {
-  constexpr int LPR = 32;
-  constexpr int BP = LPR * 16 + 16;
-  const size_t lds = (size_t)((M * (Kp + 16) + 15) / 16 * 16) + (size_t)WPB * NB * 16 * BP;
-  const unsigned blocks = (unsigned)((N + 16 * WPB - 1) / (16 * WPB));
+  constexpr int TPB = WPB / KS;
+  const size_t lds = (size_t)stream_lds_bytes(M, Kp, NB, WPB, KS);
+  const unsigned blocks = (unsigned)((N + 16 * TPB - 1) / (16 * TPB));
   if (nparts) *nparts = (int)blocks;
   constexpr int D = 1;  // steps of weights in flight (2 and 4 measured slower: VGPR pressure)
-  static bool once = (allow_lds(mfma_stream_kernel<NB, LPR, WPB, D, EPI>), true);
+  static bool once = (allow_lds(mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS>), true);
   (void)once;
-  hipLaunchKernelGGL((mfma_stream_kernel<NB, LPR, WPB, D, EPI>), dim3(blocks), dim3(64 * WPB), lds, s,
-                     Xq, xs, rs, (int)M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts);
+  hipLaunchKernelGGL((mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS>), dim3(blocks),
+                     dim3(64 * WPB), lds, s, Xq, xs, rs, (int)M, Kp, W0, s0, W1, s1, N, Y, acc_out,
+                     gh_parts);
   return hipGetLastError();
 }
 
-// Waves per block: as many as keep about 200 blocks (most of the 256 CUs
-// busy) -- more waves per block share one staged copy of the activations.
+// Tiles (16 weight rows) per block as keep about 200 blocks, most of the 256
+// CUs busy (more tiles per block share one staged copy of the activations);
+// layers with too few rows for that split K over 2 or 4 waves per tile.
 template <int NB, int EPI>
 static hipError_t stream_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                                 int64_t Kp, const uint32_t* W0, const float* s0,
                                 const uint32_t* W1, const float* s1, int64_t N, float* Y,
                                 int32_t* acc_out, float* gh_parts, int* nparts, hipStream_t s) {
-  auto fits = [&](int wpb) {
-    return M * (Kp + 16) + (int64_t)wpb * NB * 16 * (32 * 16 + 16) <= kStreamLds;
-  };
-  if (N >= 200 * 128 && fits(8))
-    return stream_go<NB, 8, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
-  if (N >= 200 * 64 && fits(4))
-    return stream_go<NB, 4, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
-  if (N >= 200 * 32 && fits(2))
-    return stream_go<NB, 2, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
-  return stream_go<NB, 1, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, s);
+  auto fits = [&](int wpb, int ks) { return stream_lds_bytes(M, Kp, NB, wpb, ks) <= kStreamLds; };
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t nsteps = (Kp + 64 * kStreamLpr - 1) / (64 * kStreamLpr);
+#define BL_STREAM_GO(WPB, KS)                                                                    \
+  return stream_go<NB, WPB, KS, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, \
+                                     nparts, s)
+  if (tiles >= 200 * 8 && fits(8, 1)) BL_STREAM_GO(8, 1);
+  if (tiles >= 200 * 4 && fits(4, 1)) BL_STREAM_GO(4, 1);
+  if (tiles >= 200 * 2 && fits(2, 1)) BL_STREAM_GO(2, 1);
+  if (tiles >= 200 || nsteps < 2) BL_STREAM_GO(1, 1);
+  if (nsteps >= 4 && fits(4, 4)) BL_STREAM_GO(4, 4);
+  if (fits(2, 2)) BL_STREAM_GO(2, 2);
+  BL_STREAM_GO(1, 1);
+#undef BL_STREAM_GO
 }
 
 template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
