@@ -216,6 +216,235 @@ __device__ __forceinline__ void unpack_word(uint32_t w, int& c0, int& c1, int& c
   c3 = (int)((w >> 6) & 0x03030303u);
 }
 
+// ---------------------------------------------------------------------------
+// Exact sum of squares, fast path.
+//
+// With bmax the largest exponent bin of the row (bin_of), every square is
+// x^2 = m^2 * 2^(2(b - 150)) = (m^2 << s) * 2^L, s = 2 (b - bmax) + 62,
+// L = 2 (bmax - 150) - 62.  Terms with s >= 0 are added exactly into a
+// 128-bit integer A (m^2 < 2^48, so a term is < 2^110 and 2^16 of them stay
+// below 2^126); terms with s < 0 keep their bits from position -s up and set
+// a flag if anything below was cut.  The true sum is T = (A + R) * 2^L with
+// 0 <= R < 2^16 (at most 2^16 terms, each losing less than one unit), and
+// R > 0 exactly when the flag is set.  All terms are non-negative, so R can
+// change the binary64 rounding of T only through a carry into the rounding
+// position; round128() reports that case (bits 16 .. rp-1 of A all ones) as
+// undecided and the caller falls back to the exponent-bin sum.  Truncation
+// happens only when the largest element is normal (m >= 2^23), and then
+// A >= 2^108, so the rounding bit sits at position 55 or above.
+struct Sum128 {
+  uint64_t lo = 0, hi = 0;
+  bool cut = false;
+};
+
+__device__ __forceinline__ void sq_add(float x, int bmax, Sum128& a) {
+  int b;
+  uint32_t m;
+  bin_of(x, b, m);
+  const uint64_t sq = (uint64_t)m * (uint64_t)m;  // < 2^48 (0 for a zero)
+  const int s = 2 * (b - bmax) + 62;              // <= 62 for every nonzero x
+  // straight-line selects: this runs once per element in latency-bound kernels
+  const int sl = s > 0 ? s : 0;
+  const int sr = s < 0 ? (-s < 63 ? -s : 63) : 0;
+  const uint64_t add_lo = s >= 0 ? (sq << sl) : (sq >> sr);
+  const uint64_t add_hi = sl > 16 ? (sq >> (64 - (sl > 16 ? sl : 17))) : 0ull;
+  a.cut |= (sq & ((1ull << sr) - 1ull)) != 0ull;
+  a.lo += add_lo;
+  a.hi += add_hi + (a.lo < add_lo ? 1ull : 0ull);
+}
+
+__device__ __forceinline__ void sum128_merge(Sum128& a, uint64_t lo, uint64_t hi, bool cut) {
+  a.lo += lo;
+  a.hi += hi + (a.lo < lo ? 1ull : 0ull);
+  a.cut |= cut;
+}
+
+// Low 64 bits of (hi:lo) >> k, 0 <= k < 128.
+__device__ __forceinline__ uint64_t shr128(uint64_t lo, uint64_t hi, int k) {
+  if (k == 0) return lo;
+  if (k < 64) return (lo >> k) | (hi << (64 - k));
+  return hi >> (k - 64);
+}
+
+// Binary64 rounding (to nearest, ties to even) of (A + R) * 2^L as described
+// above; false when R could carry into the rounding position.
+__device__ inline bool round128(const Sum128& a, int L, double* out) {
+  if (a.hi == 0ull && a.lo == 0ull) {
+    *out = 0.0;
+    return !a.cut;
+  }
+  const int P = a.hi ? 127 - __clzll((long long)a.hi) : 63 - __clzll((long long)a.lo);
+  if (P <= 52) {  // A < 2^53 is exact (no term was cut: the largest is subnormal)
+    *out = ldexp((double)a.lo, L);
+    return !a.cut;
+  }
+  const int rp = P - 53;  // position of the rounding bit
+  if (a.cut) {
+    if (rp <= 16) return false;
+    const uint64_t mid = shr128(a.lo, a.hi, 16) & ((1ull << (rp - 16)) - 1ull);
+    if (mid == (1ull << (rp - 16)) - 1ull) return false;
+  }
+  uint64_t mant = shr128(a.lo, a.hi, rp + 1) & ((1ull << 53) - 1ull);
+  const bool rnd = (shr128(a.lo, a.hi, rp) & 1ull) != 0ull;
+  bool below = a.cut;
+  if (rp >= 64)
+    below |= a.lo != 0ull || (a.hi & ((1ull << (rp - 64)) - 1ull)) != 0ull;
+  else if (rp > 0)
+    below |= (a.lo & ((1ull << rp) - 1ull)) != 0ull;
+  int e = rp + 1 + L;
+  if (rnd && (below || (mant & 1ull))) {
+    mant += 1ull;
+    if (mant == (1ull << 53)) {
+      mant >>= 1;
+      e += 1;
+    }
+  }
+  *out = ldexp((double)mant, e);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide reductions on DPP lane moves (VALU latency, a few cycles per
+// step) rather than ds_bpermute shuffles (LDS-pipe latency): quad
+// exchanges, the half-row and row mirrors, then row broadcasts 15 and 31.
+// Every lane of the wave must be active; the result is read from lane 63
+// and returned (wave-uniform) to all lanes.
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kBcast15 = 0x142;
+constexpr int kBcast31 = 0x143;
+
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ int mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWMASK, 0xF, false);
+}
+
+template <typename Op>
+__device__ __forceinline__ int reduce_i32(int v, int ident, Op op) {
+  v = op(v, mov<kXor1>(ident, v));
+  v = op(v, mov<kXor2>(ident, v));
+  v = op(v, mov<kHalfMirror>(ident, v));
+  v = op(v, mov<kMirror>(ident, v));
+  v = op(v, mov<kBcast15, 0xA>(ident, v));
+  v = op(v, mov<kBcast31, 0xC>(ident, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int sum_i32(int v) {
+  return reduce_i32(v, 0, [](int a, int b) { return a + b; });
+}
+__device__ __forceinline__ int max_i32(int v) {
+  return reduce_i32(v, INT32_MIN, [](int a, int b) { return a > b ? a : b; });
+}
+// max of non-negative floats (their bit patterns order as integers)
+__device__ __forceinline__ float max_nonneg_f32(float v) {
+  return __int_as_float(max_i32(__float_as_int(v)));
+}
+
+// 128-bit sum with a sticky flag (Sum128 above), same pattern.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ void merge_from(Sum128& a) {
+  const uint32_t l0 = (uint32_t)mov<CTRL, ROWMASK>(0, (int)(uint32_t)a.lo);
+  const uint32_t l1 = (uint32_t)mov<CTRL, ROWMASK>(0, (int)(uint32_t)(a.lo >> 32));
+  const uint32_t h0 = (uint32_t)mov<CTRL, ROWMASK>(0, (int)(uint32_t)a.hi);
+  const uint32_t h1 = (uint32_t)mov<CTRL, ROWMASK>(0, (int)(uint32_t)(a.hi >> 32));
+  const int c = mov<CTRL, ROWMASK>(0, (int)a.cut);
+  sum128_merge(a, (uint64_t)l0 | ((uint64_t)l1 << 32), (uint64_t)h0 | ((uint64_t)h1 << 32), c != 0);
+}
+__device__ __forceinline__ Sum128 sum128(Sum128 a) {
+  merge_from<kXor1>(a);
+  merge_from<kXor2>(a);
+  merge_from<kHalfMirror>(a);
+  merge_from<kMirror>(a);
+  merge_from<kBcast15, 0xA>(a);
+  merge_from<kBcast31, 0xC>(a);
+  Sum128 r;
+  r.lo = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.lo, 63) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.lo >> 32), 63) << 32);
+  r.hi = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a.hi, 63) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a.hi >> 32), 63) << 32);
+  r.cut = __builtin_amdgcn_readlane((int)a.cut, 63) != 0;
+  return r;
+}
+}  // namespace dpp
+
+// Exact binary64 rounding of the sum of squares of a block's row (NT
+// threads), values held in registers, NWT words of 4 per thread.  Fast path
+// as above; the exponent-bin sum when the rounding is undecided.
+struct SumsqScratch {
+  unsigned long long bins[4][kBins];
+  uint64_t tot[kBins];
+  unsigned long long limbs[kLimbs];
+  uint64_t part[16][2];
+  double res;
+  int pcut[16];
+  int bmax[16];
+};
+
+template <int NWT, int NT>
+__device__ double block_sumsq_exact(const float (&xv)[NWT][4], SumsqScratch& sh) {
+  constexpr int NWV = NT / 64;
+  static_assert(NWV >= 1 && NWV <= 16, "block size");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int bmax = 0;
+#pragma unroll
+  for (int j = 0; j < NWT; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int bb;
+      uint32_t mm;
+      bin_of(xv[j][b], bb, mm);
+      bmax = mm ? max(bmax, bb) : bmax;
+    }
+  bmax = dpp::max_i32(bmax);
+  if (lane == 0) sh.bmax[wave] = bmax;
+  __syncthreads();
+  // second level: every wave combines the per-wave values itself
+  bmax = dpp::max_i32(lane < NWV ? sh.bmax[lane] : 0);
+  Sum128 acc;
+#pragma unroll
+  for (int j = 0; j < NWT; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sq_add(xv[j][b], bmax, acc);
+  acc = dpp::sum128(acc);
+  if (lane == 0) {
+    sh.part[wave][0] = acc.lo;
+    sh.part[wave][1] = acc.hi;
+    sh.pcut[wave] = acc.cut;
+  }
+  __syncthreads();
+  Sum128 t;
+  if (lane < NWV) {
+    t.lo = sh.part[lane][0];
+    t.hi = sh.part[lane][1];
+    t.cut = sh.pcut[lane] != 0;
+  }
+  t = dpp::sum128(t);
+  double s = 0.0;
+  const bool ok = round128(t, 2 * (bmax - 150) - 62, &s);  // same in every thread
+  if (!ok) {  // block-uniform
+    for (int i = tid; i < 4 * kBins; i += NT) (&sh.bins[0][0])[i] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NWT; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        int bb;
+        uint32_t mm;
+        bin_of(xv[j][b], bb, mm);
+        if (mm) atomicAdd(&sh.bins[wave & 3][bb], (unsigned long long)mm * (unsigned long long)mm);
+      }
+    __syncthreads();
+    for (int b = tid; b < kBins; b += NT)
+      sh.tot[b] = sh.bins[0][b] + sh.bins[1][b] + sh.bins[2][b] + sh.bins[3][b];
+    __syncthreads();
+    s = finalize_bins<2>(sh.tot, sh.limbs, &sh.res);
+  }
+  return s;
+}
+
 // sum over the 16 weights of one word of code * x, x given as 4 words of 4
 // int8 in natural order.  Three of the four fields are used in place (scaled
 // by 4 and 16) and rescaled exactly afterwards; all values stay < 2^7 per

@@ -30,7 +30,7 @@ hipError_t launch_gemv(const int8_t* Xq, const float* x_scale, const int32_t* ro
                        int32_t* acc_out, hipStream_t s);
 
 // One token from float activations: quantise inside the GEMV (every block
-// redoes the row into LDS) -- one launch.  Needs bl_padded_k(K) <= 16384
+// redoes the row into LDS) -- one launch.  Needs bl_padded_k(K) <= 7168
 // (gemv_fused_ok).  xq_out/xs_out/rs_out (optional) receive the codes.
 bool gemv_fused_ok(int64_t K);
 hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t* Wp,

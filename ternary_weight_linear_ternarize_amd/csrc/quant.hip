@@ -8,31 +8,32 @@
 // RMSNorm kernel below makes the mean square exact and order-free (integer
 // exponent bins of m^2, rounded once to binary64).
 //
-// One 256-thread block per token row.  Codes are written four per 32-bit
+// One block per token row (256 threads, 1024 for few rows).  Codes are written four per 32-bit
 // store into rows of Kp bytes; the padding columns get code 0.
 #include "bl_device.h"
 #include "bl_launch.h"
 
 namespace bl {
 
+// Block-wide max (of non-negative values) / sum; blockDim.x a multiple of 64,
+// at most 1024; red holds 16 entries.  Wave level on DPP moves, then every
+// wave combines the per-wave values itself (no serial loop).
 __device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = dpp::max_nonneg_f32(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwv = blockDim.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  v = dpp::max_nonneg_f32(lane < nwv ? red[lane] : 0.0f);
   __syncthreads();
   return v;
 }
 
 __device__ __forceinline__ int block_sum(int v, int* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = dpp::sum_i32(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nwv = blockDim.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  v = red[0] + red[1] + red[2] + red[3];
+  v = dpp::sum_i32(lane < nwv ? red[lane] : 0);
   __syncthreads();
   return v;
 }
@@ -59,16 +60,16 @@ __device__ __forceinline__ int write_codes(F f, int64_t K, int64_t Kp, const Qua
   return rs;
 }
 
-// Loads words tid, tid+256, ... (four consecutive elements each) of a row
+// Loads words tid, tid+NT, ... (four consecutive elements each) of a row
 // into registers; elements past K read as 0.
-template <bool BF16, int NWT>
+template <bool BF16, int NWT, int NT>
 __device__ __forceinline__ void load_row_words(const char* base, int64_t K, int64_t nw,
                                                float (&xv)[NWT][4]) {
   const int tid = threadIdx.x;
   const bool vec = !BF16 && (K & 3) == 0;
 #pragma unroll
   for (int j = 0; j < NWT; ++j) {
-    const int64_t wd = tid + 256 * j;
+    const int64_t wd = tid + NT * j;
     if (vec && 4 * wd + 3 < K) {
       const float4 v = *reinterpret_cast<const float4*>(base + 16 * wd);
       xv[j][0] = v.x; xv[j][1] = v.y; xv[j][2] = v.z; xv[j][3] = v.w;
@@ -84,13 +85,13 @@ __device__ __forceinline__ void load_row_words(const char* base, int64_t K, int6
 
 // Writes the codes of the register-held row words and returns this thread's
 // share of their sum.
-template <int NWT>
+template <int NWT, int NT>
 __device__ __forceinline__ int store_row_codes(const float (&xv)[NWT][4], int64_t nw,
                                                const QuantDiv& d, int8_t* q) {
   int rs = 0;
 #pragma unroll
   for (int j = 0; j < NWT; ++j) {
-    const int64_t wd = threadIdx.x + 256 * j;
+    const int64_t wd = threadIdx.x + NT * j;
     if (wd < nw) {
       uint32_t pk = 0u;
 #pragma unroll
@@ -105,17 +106,19 @@ __device__ __forceinline__ int store_row_codes(const float (&xv)[NWT][4], int64_
   return rs;
 }
 
-// NWT > 0: the row (Kp <= 1024 * NWT) is held in registers and read once.
-// NWT == 0: any length, the row is read twice.
-template <bool BF16, int NWT>
-__global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__ X, int64_t K,
+// NT threads per row.  NWT > 0: the row (Kp <= 4 NT NWT) is held in
+// registers and read once; NWT == 0: any length, the row is read twice.
+// Few rows take NT = 1024: these kernels are latency-bound, and a wave's
+// time is its instruction count, so the row is spread over more waves.
+template <bool BF16, int NWT, int NT>
+__global__ __launch_bounds__(NT) void act_quant_kernel(const void* __restrict__ X, int64_t K,
                                                         int64_t Kp, int8_t* __restrict__ Xq,
                                                         float* __restrict__ x_scale,
                                                         int32_t* __restrict__ rowsum,
                                                         const float* __restrict__ gamma_parts,
                                                         int nparts, int64_t M) {
-  __shared__ float redf[4];
-  __shared__ int redi[4];
+  __shared__ float redf[16];
+  __shared__ int redi[16];
   const int64_t m = blockIdx.x;
   const char* base = reinterpret_cast<const char*>(X) + m * K * (BF16 ? 2 : 4);
   float g = 0.0f;
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
   int rs;
   if constexpr (NWT > 0) {
     float xv[NWT][4];
-    load_row_words<BF16, NWT>(base, K, Kp / 4, xv);
+    load_row_words<BF16, NWT, NT>(base, K, Kp / 4, xv);
     if (!gamma_parts) {
 #pragma unroll
       for (int j = 0; j < NWT; ++j)
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
         for (int b = 0; b < 4; ++b) g = fmaxf(g, fabsf(xv[j][b]));
     }
     g = block_max(g, redf);
-    rs = store_row_codes<NWT>(xv, Kp / 4, make_qdiv(g), Xq + m * Kp);
+    rs = store_row_codes<NWT, NT>(xv, Kp / 4, make_qdiv(g), Xq + m * Kp);
   } else {
     if (!gamma_parts) {
       for (int64_t k = threadIdx.x; k < K; k += blockDim.x) g = fmaxf(g, fabsf(load_act<BF16>(base, k)));
@@ -153,44 +156,43 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const void* __restrict__
 // r = 1 / sqrt(ms + eps), ms = binary32(binary64(exact sum x^2) / D).
 // NWT > 0: the row (Dp <= 1024 * NWT) is held in registers; NWT == 0: any
 // length, the row is re-read from memory for each pass.
-template <bool BF16, int NWT>
-__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
+template <bool BF16, int NWT, int NT>
+__global__ __launch_bounds__(NT) void rmsnorm_quant_kernel(
     const void* __restrict__ H, int64_t D, int64_t Dp, const float* __restrict__ norm_w,
     float eps, float* __restrict__ xn, int8_t* __restrict__ Xq, float* __restrict__ x_scale,
     int32_t* __restrict__ rowsum) {
   constexpr int NR = NWT > 0 ? NWT : 1;
-  __shared__ unsigned long long bins[4][kBins];
-  __shared__ uint64_t tot[kBins];
-  __shared__ unsigned long long limbs[kLimbs];
-  __shared__ double res;
-  __shared__ float redf[4];
-  __shared__ int redi[4];
+  __shared__ float redf[16];
+  __shared__ int redi[16];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t m = blockIdx.x;
   const char* base = reinterpret_cast<const char*>(H) + m * D * (BF16 ? 2 : 4);
   const int64_t nw = Dp / 4;
   float xv[NR][4];
-  if constexpr (NWT > 0) load_row_words<BF16, NWT>(base, D, nw, xv);
-  for (int i = tid; i < 4 * kBins; i += 256) (&bins[0][0])[i] = 0ull;
-  __syncthreads();
-  auto add_bin = [&](float v) {
-    int bb;
-    uint32_t mm;
-    bin_of(v, bb, mm);
-    if (mm) atomicAdd(&bins[wave][bb], (unsigned long long)mm * (unsigned long long)mm);
-  };
+  double s = 0.0;
   if constexpr (NWT > 0) {
-#pragma unroll
-    for (int j = 0; j < NWT; ++j)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) add_bin(xv[j][b]);
+    load_row_words<BF16, NWT, NT>(base, D, nw, xv);
+    __shared__ SumsqScratch sh;
+    s = block_sumsq_exact<NWT, NT>(xv, sh);
   } else {
-    for (int64_t k = tid; k < D; k += 256) add_bin(load_act<BF16>(base, k));
+    // rows longer than 16384: exponent bins over reloaded values
+    __shared__ unsigned long long bins[4][kBins];
+    __shared__ uint64_t tot[kBins];
+    __shared__ unsigned long long limbs[kLimbs];
+    __shared__ double res;
+    for (int i = tid; i < 4 * kBins; i += NT) (&bins[0][0])[i] = 0ull;
+    __syncthreads();
+    for (int64_t k = tid; k < D; k += NT) {
+      int bb;
+      uint32_t mm;
+      bin_of(load_act<BF16>(base, k), bb, mm);
+      if (mm) atomicAdd(&bins[wave & 3][bb], (unsigned long long)mm * (unsigned long long)mm);
+    }
+    __syncthreads();
+    for (int b = tid; b < kBins; b += NT) tot[b] = bins[0][b] + bins[1][b] + bins[2][b] + bins[3][b];
+    __syncthreads();
+    s = finalize_bins<2>(tot, limbs, &res);
   }
-  __syncthreads();
-  for (int b = tid; b < kBins; b += 256) tot[b] = bins[0][b] + bins[1][b] + bins[2][b] + bins[3][b];
-  __syncthreads();
-  const double s = finalize_bins<2>(tot, limbs, &res);
   const float ms = (float)(s / (double)D);
   // __builtin_sqrtf is correctly rounded under -fhip-fp32-correctly-rounded-divide-sqrt
   // (the __fsqrt_rn intrinsic maps to a native approximation on this toolchain).
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   if constexpr (NWT > 0) {
 #pragma unroll
     for (int j = 0; j < NWT; ++j) {
-      const int64_t wd = tid + 256 * j;
+      const int64_t wd = tid + NT * j;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int64_t k = 4 * wd + b;
@@ -216,9 +218,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
       }
     }
     g = block_max(g, redf);
-    rs = store_row_codes<NWT>(xv, nw, make_qdiv(g), Xq + m * Dp);
+    rs = store_row_codes<NWT, NT>(xv, nw, make_qdiv(g), Xq + m * Dp);
   } else {
-    for (int64_t k = tid; k < D; k += 256) {
+    for (int64_t k = tid; k < D; k += NT) {
       const float v = norm(load_act<BF16>(base, k), k);
       xn[m * D + k] = v;
       g = fmaxf(g, fabsf(v));
@@ -234,51 +236,72 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(
   }
 }
 
-template <int NWT>
+template <int NWT, int NT>
 static void act_quant_go(const void* X, bool bf16, int64_t M, int64_t K, int64_t Kp, int8_t* Xq,
                          float* x_scale, int32_t* rowsum, const float* gamma_parts, int nparts,
                          hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL((act_quant_kernel<true, NWT>), dim3((unsigned)M), dim3(256), 0, s, X, K, Kp,
-                       Xq, x_scale, rowsum, gamma_parts, nparts, M);
+    hipLaunchKernelGGL((act_quant_kernel<true, NWT, NT>), dim3((unsigned)M), dim3(NT), 0, s, X, K,
+                       Kp, Xq, x_scale, rowsum, gamma_parts, nparts, M);
   else
-    hipLaunchKernelGGL((act_quant_kernel<false, NWT>), dim3((unsigned)M), dim3(256), 0, s, X, K, Kp,
-                       Xq, x_scale, rowsum, gamma_parts, nparts, M);
+    hipLaunchKernelGGL((act_quant_kernel<false, NWT, NT>), dim3((unsigned)M), dim3(NT), 0, s, X, K,
+                       Kp, Xq, x_scale, rowsum, gamma_parts, nparts, M);
 }
+
+// Rows of up to 64 tokens run 1024 threads per row (see act_quant_kernel).
+constexpr int64_t kWideRows = 64;
 
 hipError_t launch_act_quant(const void* X, bool bf16, int64_t M, int64_t K, int8_t* Xq,
                             float* x_scale, int32_t* rowsum, const float* gamma_parts,
                             int nparts, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (Kp <= 1024) act_quant_go<1>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
-  else if (Kp <= 3072) act_quant_go<3>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
-  else if (Kp <= 8192) act_quant_go<8>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
-  else if (Kp <= 16384) act_quant_go<16>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
-  else act_quant_go<0>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s);
+#define BL_AQ(NWT, NT) act_quant_go<NWT, NT>(X, bf16, M, K, Kp, Xq, x_scale, rowsum, gamma_parts, nparts, s)
+  if (M <= kWideRows) {
+    if (Kp <= 4096) BL_AQ(1, 1024);
+    else if (Kp <= 8192) BL_AQ(2, 1024);
+    else if (Kp <= 16384) BL_AQ(4, 1024);
+    else BL_AQ(0, 1024);
+  } else {
+    if (Kp <= 1024) BL_AQ(1, 256);
+    else if (Kp <= 3072) BL_AQ(3, 256);
+    else if (Kp <= 8192) BL_AQ(8, 256);
+    else if (Kp <= 16384) BL_AQ(16, 256);
+    else BL_AQ(0, 256);
+  }
+#undef BL_AQ
   return hipGetLastError();
 }
 
-template <int NWT>
+template <int NWT, int NT>
 static void rmsnorm_go(const void* H, bool bf16, int64_t M, int64_t D, int64_t Dp,
                        const float* norm_w, float eps, float* xn, int8_t* Xq, float* x_scale,
                        int32_t* rowsum, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL((rmsnorm_quant_kernel<true, NWT>), dim3((unsigned)M), dim3(256), 0, s, H, D,
-                       Dp, norm_w, eps, xn, Xq, x_scale, rowsum);
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<true, NWT, NT>), dim3((unsigned)M), dim3(NT), 0, s, H,
+                       D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum);
   else
-    hipLaunchKernelGGL((rmsnorm_quant_kernel<false, NWT>), dim3((unsigned)M), dim3(256), 0, s, H, D,
-                       Dp, norm_w, eps, xn, Xq, x_scale, rowsum);
+    hipLaunchKernelGGL((rmsnorm_quant_kernel<false, NWT, NT>), dim3((unsigned)M), dim3(NT), 0, s, H,
+                       D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum);
 }
 
 hipError_t launch_rmsnorm_quant(const void* H, bool bf16, int64_t M, int64_t D,
                                 const float* norm_w, float eps, float* xn, int8_t* Xq,
                                 float* x_scale, int32_t* rowsum, hipStream_t s) {
   const int64_t Dp = (D + 63) / 64 * 64;
-  if (Dp <= 1024) rmsnorm_go<1>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
-  else if (Dp <= 3072) rmsnorm_go<3>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
-  else if (Dp <= 8192) rmsnorm_go<8>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
-  else if (Dp <= 16384) rmsnorm_go<16>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
-  else rmsnorm_go<0>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s);
+#define BL_RN(NWT, NT) rmsnorm_go<NWT, NT>(H, bf16, M, D, Dp, norm_w, eps, xn, Xq, x_scale, rowsum, s)
+  // longer rows re-read the input rather than hold it (register pressure of
+  // the exact sum of squares)
+  if (M <= kWideRows) {
+    if (Dp <= 4096) BL_RN(1, 1024);
+    else if (Dp <= 8192) BL_RN(2, 1024);
+    else BL_RN(0, 1024);
+  } else {
+    if (Dp <= 1024) BL_RN(1, 256);
+    else if (Dp <= 3072) BL_RN(3, 256);
+    else if (Dp <= 8192) BL_RN(8, 256);
+    else BL_RN(0, 256);
+  }
+#undef BL_RN
   return hipGetLastError();
 }
 
