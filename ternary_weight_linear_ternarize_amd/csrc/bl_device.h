@@ -338,6 +338,31 @@ __device__ __forceinline__ int sum_i32(int v) {
 __device__ __forceinline__ int max_i32(int v) {
   return reduce_i32(v, INT32_MIN, [](int a, int b) { return a > b ? a : b; });
 }
+// Value of lane (lane ^ O) for O = 1 .. 32: quad permutes, row rotations
+// (row_ror:n moves lane i - n to lane i within a row of 16) and the gfx950
+// row/half swaps, all VALU ops.
+template <int O>
+__device__ __forceinline__ int xchg(int v) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "stride");
+  if constexpr (O == 1) {
+    return mov<kXor1>(0, v);
+  } else if constexpr (O == 2) {
+    return mov<kXor2>(0, v);
+  } else if constexpr (O == 4) {
+    // banks 0, 2 take lane i + 4 (row_ror:12), banks 1, 3 take lane i - 4 (row_ror:4)
+    const int r = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0x5, false);
+    return __builtin_amdgcn_update_dpp(r, v, 0x124, 0xF, 0xA, false);
+  } else if constexpr (O == 8) {
+    return mov<0x128>(0, v);  // row_ror:8
+  } else if constexpr (O == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 16) ? p[0] : p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 32) ? p[0] : p[1]);
+  }
+}
+
 // max of non-negative floats (their bit patterns order as integers)
 __device__ __forceinline__ float max_nonneg_f32(float v) {
   return __int_as_float(max_i32(__float_as_int(v)));

@@ -26,6 +26,8 @@
 //            (identical bits) into LDS -- one launch per layer;
 //   XS_PARTS float activations whose scale is the maximum of per-block partial
 //            maxima written by the previous kernel (the FFN's h).
+#include <type_traits>
+
 #include "bl_device.h"
 #include "bl_launch.h"
 
@@ -36,46 +38,61 @@ enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3 };
 
 constexpr int kFusedMaxKp = 7168;  // largest padded K quantised inside the GEMV
 
-// Reduce v[0..R) (per-lane partials of R rows) across the 64 lanes.  On
-// return lane l holds the full sum of row (l >> (6 - log2 R)) in v[0].
+// Reduce v[0..R) (per-lane partials of R rows) across the 64 lanes with a
+// transposing butterfly on DPP / lane-swap moves, small strides first: the
+// first log2 R steps exchange halves of the row set, the rest add.  On return
+// every lane l holds the full sum of row gemv_row<R>(l) in v[0] (the low
+// log2 R bits of l, bit-reversed).
 template <int R>
 __device__ __forceinline__ int wave_transpose_reduce(int (&v)[R]) {
   const int lane = threadIdx.x & 63;
   int cnt = R;
-  int o = 32;
-#pragma unroll
-  for (int step = 0; step < 6; ++step) {
+  auto step = [&](auto o_tag) {
+    constexpr int O = decltype(o_tag)::value;
     if (cnt > 1) {
       const int half = cnt >> 1;
-      const bool hi = (lane & o) != 0;
+      const bool hi = (lane & O) != 0;
 #pragma unroll
       for (int i = 0; i < R / 2; ++i) {
         if (i < half) {
           const int keep = hi ? v[half + i] : v[i];
           const int send = hi ? v[i] : v[half + i];
-          v[i] = keep + __shfl_xor(send, o);
+          v[i] = keep + dpp::xchg<O>(send);
         }
       }
       cnt = half;
     } else {
-      v[0] += __shfl_xor(v[0], o);
+      v[0] += dpp::xchg<O>(v[0]);
     }
-    o >>= 1;
-  }
+  };
+  step(std::integral_constant<int, 1>());
+  step(std::integral_constant<int, 2>());
+  step(std::integral_constant<int, 4>());
+  step(std::integral_constant<int, 8>());
+  step(std::integral_constant<int, 16>());
+  step(std::integral_constant<int, 32>());
   return v[0];
 }
 
-__device__ __forceinline__ float block_max4(float v, float* red) {
+// Row whose total lane l holds after wave_transpose_reduce<R>.
+template <int R>
+__device__ __forceinline__ int gemv_row(int lane) {
+  constexpr int LOGR = (R == 1) ? 0 : (R == 2) ? 1 : (R == 4) ? 2 : (R == 8) ? 3 : 4;
+  int r = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int b = 0; b < LOGR; ++b) r |= ((lane >> b) & 1) << (LOGR - 1 - b);
+  return r;
+}
+
+__device__ __forceinline__ float block_max4(float v, float* red) {
+  v = dpp::max_nonneg_f32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 __device__ __forceinline__ int block_sum4(int v, int* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = dpp::sum_i32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return red[0] + red[1] + red[2] + red[3];
@@ -182,11 +199,10 @@ template <int R, int EPI>
 __device__ __forceinline__ float gemv_epilogue(const GemvArgs& a, int64_t rb, int (&part)[R],
                                                int rsum, float gx, float sw0, float sw1) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;
-  constexpr int LOGR = (R == 1) ? 0 : (R == 2) ? 1 : (R == 4) ? 2 : (R == 8) ? 3 : 4;
   const int lane = threadIdx.x & 63;
   const int sum = wave_transpose_reduce<R>(part);
-  const int row = lane >> (6 - LOGR);
-  const bool leader = (lane & ((64 >> LOGR) - 1)) == 0;
+  const int row = gemv_row<R>(lane);
+  const bool leader = lane < R;  // one lane per row
   const int acc = sum - rsum;
   const int64_t n = rb * RW + row;
   if constexpr (EPI == EPI_STORE) {
@@ -196,9 +212,9 @@ __device__ __forceinline__ float gemv_epilogue(const GemvArgs& a, int64_t rb, in
     }
     return 0.0f;
   } else {
-    // rows [0, RW) are gate, [RW, R) are up; bring up's sum next to gate's
-    constexpr int SPAN = 64 >> LOGR;  // lanes per row
-    const int acc_up = __shfl(acc, (lane + RW * SPAN) & 63);
+    // rows [0, RW) are gate, [RW, R) are up: up row g + RW sits in the lane
+    // next to gate row g (row index g + RW bit-reversed differs in bit 0)
+    const int acc_up = dpp::xchg<1>(acc);
     float hm = 0.0f;
     if (leader && row < RW && n < a.N) {
       const float gv = dequant(acc, __fmul_rn(sw0, gx));
@@ -329,8 +345,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   if (rb * RW < a.N) hmax = gemv_epilogue<R, EPI>(a, rb, part, rsum, gx, sw0, sw1);
 
   if constexpr (EPI == EPI_GATEUP) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+    hmax = dpp::max_nonneg_f32(hmax);
     __shared__ float redh[4];
     if (lane == 0) redh[wave] = hmax;
     __syncthreads();
