@@ -30,6 +30,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# HBM bytes per launch of the dominant kernel from rocprofv3 counters
+# (profiles/gemv_fused_decode_2b.md: FETCH_SIZE x 1.9998 + WRITE_SIZE, the
+# factors a plain 256 MiB copy reads back).  Valid for this kernel build
+# only: set to None whenever the kernel changes until the counters are
+# taken again.
+UP_GEMV_KERNEL = "gemv_kernel<1,4,0,1>"
+UP_GEMV_TRAFFIC_BYTES = 4_661_000
+
 METRIC = ("BitLinear W1.58A8: decode GEMV weight GB/s (% HBM peak); "
           "prefill int8 TOPS (% MFMA)")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -263,8 +271,9 @@ def main():
     alg_dn = pbytes + N * 4 + 4 + K * 4
     achieved = alg_up / (up_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemv_kernel<1,8,0,1> (fused quant + GEMV, 2560->6912, M=1)",
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": UP_GEMV_TRAFFIC_BYTES,
+                "kernel": UP_GEMV_KERNEL + " (fused quant + GEMV, 2560->6912, M=1)",
                 "avg_us": round(up_ms * 1e3, 3), "algorithmic_bytes": alg_up}
     kernels = {
         "gemv_fused_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3), "GBps": round(achieved, 1)},
