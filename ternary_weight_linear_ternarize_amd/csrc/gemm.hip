@@ -529,11 +529,10 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
-  if (M <= 32)
-    return mfma_launch<2, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
-                                             acc_out, nullptr, nullptr, s);
+  // 17 <= M <= 64: 32 x 32 block tiles (four 16 x 16 wave tiles) keep more
+  // blocks in flight than 64-row tiles for these weight-streaming shapes
   if (M <= 64)
-    return mfma_launch<4, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+    return mfma_launch<1, 1, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
   return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                            acc_out, nullptr, nullptr, s);
@@ -556,11 +555,9 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                               gh_parts, nparts, s);
-  if (M <= 32)
-    return mfma_launch<2, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
-                                              gh_parts, nparts, s);
+  // 17 <= M <= 64: 64 x 16 block tiles (waves split the token rows)
   if (M <= 64)
-    return mfma_launch<4, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+    return mfma_launch<1, 1, 4, 1, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                               gh_parts, nparts, s);
   return mfma_launch<4, 4, 2, 2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                             gh_parts, nparts, s);
