@@ -393,6 +393,26 @@ __device__ __forceinline__ Sum128 sum128(Sum128 a) {
   r.cut = __builtin_amdgcn_readlane((int)a.cut, 63) != 0;
   return r;
 }
+// sum of doubles, same pattern
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ double movd(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)mov<CTRL, ROWMASK>(0, (int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)mov<CTRL, ROWMASK>(0, (int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((uint64_t)lo | ((uint64_t)hi << 32)));
+}
+__device__ __forceinline__ double sum_f64(double v) {
+  v += movd<kXor1>(v);
+  v += movd<kXor2>(v);
+  v += movd<kHalfMirror>(v);
+  v += movd<kMirror>(v);
+  v += movd<kBcast15, 0xA>(v);
+  v += movd<kBcast31, 0xC>(v);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)((uint64_t)lo | ((uint64_t)hi << 32)));
+}
 }  // namespace dpp
 
 // Exact binary64 rounding of the sum of squares of a block's row (NT
@@ -468,6 +488,47 @@ __device__ double block_sumsq_exact(const float (&xv)[NWT][4], SumsqScratch& sh)
     s = finalize_bins<2>(sh.tot, sh.limbs, &sh.res);
   }
   return s;
+}
+
+// Mean square of a block's row for RMSNorm: ms = binary32(binary64(S) / D)
+// with S the exact sum of squares (NT threads, values in registers).
+//
+// Fast path: S_a = the binary64 sum of the squares (each square is exact in
+// binary64) in any order, |S_a - S| <= (n - 1) 2^-53 S <= 2^-37 S for
+// n <= 2^16 non-negative terms, and q_a = RN64(S_a / D).  If q_a is farther
+// than 2^-35 q_a from both binary32 rounding midpoints around c = RN32(q_a),
+// then S / D and every value within 2^-36 of it (the exact route's
+// intermediate binary64 roundings included) round to c, so ms = c.  Otherwise
+// (rows within ~2^-35 of a midpoint, all zero, or at the top of the range)
+// the exact sum decides.
+template <int NWT, int NT>
+__device__ float block_meansq(const float (&xv)[NWT][4], int64_t D, SumsqScratch& sh) {
+  constexpr int NWV = NT / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double a = 0.0;
+#pragma unroll
+  for (int j = 0; j < NWT; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const double x = (double)xv[j][b];
+      a += x * x;
+    }
+  a = dpp::sum_f64(a);
+  double* dpart = reinterpret_cast<double*>(&sh.part[0][0]);
+  if (lane == 0) dpart[wave] = a;
+  __syncthreads();
+  a = dpp::sum_f64(lane < NWV ? dpart[lane] : 0.0);
+  const double qa = a / (double)D;
+  const float c = (float)qa;
+  // neighbours of c >= 0 (c = 0 gives a NaN below, hence the exact path)
+  const uint32_t cb = __float_as_uint(c);
+  const double lo = 0.5 * ((double)c + (double)__uint_as_float(cb - 1u));
+  const double hi = 0.5 * ((double)c + (double)__uint_as_float(cb + 1u));
+  const double tol = qa * 0x1p-35;
+  __syncthreads();  // dpart (sh.part) is reused below
+  if (cb < 0x7f7fffffu && qa - lo > tol && hi - qa > tol) return c;  // block-uniform
+  const double s = block_sumsq_exact<NWT, NT>(xv, sh);
+  return (float)(s / (double)D);
 }
 
 // sum over the 16 weights of one word of code * x, x given as 4 words of 4

@@ -169,11 +169,11 @@ __global__ __launch_bounds__(NT) void rmsnorm_quant_kernel(
   const char* base = reinterpret_cast<const char*>(H) + m * D * (BF16 ? 2 : 4);
   const int64_t nw = Dp / 4;
   float xv[NR][4];
-  double s = 0.0;
+  float ms;
   if constexpr (NWT > 0) {
     load_row_words<BF16, NWT, NT>(base, D, nw, xv);
     __shared__ SumsqScratch sh;
-    s = block_sumsq_exact<NWT, NT>(xv, sh);
+    ms = block_meansq<NWT, NT>(xv, D, sh);
   } else {
     // rows longer than 16384: exponent bins over reloaded values
     __shared__ unsigned long long bins[4][kBins];
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(NT) void rmsnorm_quant_kernel(
     __syncthreads();
     for (int b = tid; b < kBins; b += NT) tot[b] = bins[0][b] + bins[1][b] + bins[2][b] + bins[3][b];
     __syncthreads();
-    s = finalize_bins<2>(tot, limbs, &res);
+    const double s = finalize_bins<2>(tot, limbs, &res);
+    ms = (float)(s / (double)D);
   }
-  const float ms = (float)(s / (double)D);
   // __builtin_sqrtf is correctly rounded under -fhip-fp32-correctly-rounded-divide-sqrt
   // (the __fsqrt_rn intrinsic maps to a native approximation on this toolchain).
   const float r = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(ms, eps)));

@@ -1,4 +1,4 @@
-"""Host check of the fast exact sum of squares used by the RMSNorm kernel
+"""Host checks of the RMSNorm mean square: the fast exact sum of squares
 (quant.hip: sq_add, round128).  The kernel adds every x^2 as an integer
 relative to the row's largest exponent bin, in 128 bits, cutting the bits of
 very small terms below the unit and flagging the cut; it then rounds to
@@ -146,3 +146,70 @@ def test_rounding_step_is_safe_for_every_cut_value():
         for r in (1, (1 << 16) - 1):
             assert v == float(Fraction(a + r) * Fraction(2) ** L)
     assert decided > 2000 and undecided > 500
+
+
+# ---------------------------------------------------------------------------
+# The RMSNorm mean square (bl_device.h, block_meansq): a binary64 sum of the
+# squares decides ms = binary32(binary64(S) / D) directly unless S / D lies
+# within 2^-35 of a binary32 rounding midpoint; then the exact sum decides.
+
+def meansq_fast(row, rng):
+    """(decided, value) as the kernel's fast path computes them, with the
+    binary64 additions in a random order (the kernel's order differs)."""
+    sq = np.asarray(row, np.float64) ** 2
+    a = 0.0
+    for v in sq[rng.permutation(len(sq))]:
+        a += float(v)
+    D = len(row)
+    qa = a / D
+    with np.errstate(over="ignore"):
+        c = np.float32(qa)
+    cb = int(c.view(np.uint32))
+    if not np.isfinite(c) or cb == 0 or cb >= 0x7F7FFFFF:
+        return False, None
+    lo = 0.5 * (float(c) + float(np.uint32(cb - 1).view(np.float32)))
+    hi = 0.5 * (float(c) + float(np.uint32(cb + 1).view(np.float32)))
+    tol = qa * 2.0 ** -35
+    if qa - lo > tol and hi - qa > tol:
+        return True, float(c)
+    return False, None
+
+
+def meansq_exact(row):
+    s = float(sum(Fraction(float(x)) ** 2 for x in row))  # RN64 of the exact sum
+    return float(np.float32(s / len(row)))  # RN64 of the quotient, then RN32
+
+
+def near_midpoint_rows(rng, count, D=2560):
+    """Rows whose exact mean square is pushed onto a binary32 midpoint, or to
+    a few times the tolerance on either side of it, by re-solving the largest
+    and then a small element: the fast path must not decide them wrongly."""
+    offsets = [0, 0, 2.0 ** -34, -(2.0 ** -34), 2.0 ** -33, -(2.0 ** -33), 2.0 ** -30, -(2.0 ** -30)]
+    for t in range(count):
+        row = rng.standard_normal(D).astype(np.float32)
+        S = sum(Fraction(float(x)) ** 2 for x in row)
+        q = S / D
+        c = np.float32(float(q))
+        cb = int(c.view(np.uint32))
+        mid = (Fraction(float(c)) + Fraction(float(np.uint32(cb + 1).view(np.float32)))) / 2
+        mid *= 1 + Fraction(offsets[t % len(offsets)])
+        # coarse: the largest element; fine: a small one (finer binary32 steps)
+        for i in (int(np.argmax(np.abs(row))), int(np.argmin(np.abs(row) + (np.abs(row) < 1e-3)))):
+            S = sum(Fraction(float(x)) ** 2 for x in row)
+            want = Fraction(float(row[i])) ** 2 + (mid * D - S)
+            row[i] = np.float32(np.sqrt(float(max(want, Fraction(0)))))
+        yield row
+
+
+def test_mean_square_fast_path_never_decides_wrongly():
+    rng = np.random.default_rng(5)
+    decided = undecided = 0
+    cases = list(near_midpoint_rows(rng, 60)) + [r for r in rows() if np.any(r)]
+    for row in cases:
+        ok, v = meansq_fast(row, rng)
+        if ok:
+            decided += 1
+            assert v == meansq_exact(row)
+        else:
+            undecided += 1
+    assert decided >= 20 and undecided >= 15
