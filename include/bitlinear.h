@@ -187,10 +187,12 @@ int bitlinear_forward_fused(const void *X, int dtype, int64_t M, int64_t K, cons
  *   H   float [M][F]   relu(gate)^2 * up
  *   GH  float [M]      max |h| per token (stored as float bits)
  *   QH  int8  [M][Fp]  int8 codes of h;  RSH int32 [M] row sums
- *   GHP float [P][M]   per-block partial maxima of |h| (scratch)          */
+ *   GHP float [P][M]   per-block partial maxima of |h| (scratch)
+ *   PART int32         split-K partial sums of the down projection for
+ *                      17..64 tokens (scratch; size 0 otherwise)           */
 enum {
     BL_FFN_WS_XN = 0, BL_FFN_WS_QX, BL_FFN_WS_GX, BL_FFN_WS_RSX, BL_FFN_WS_H,
-    BL_FFN_WS_GH, BL_FFN_WS_QH, BL_FFN_WS_RSH, BL_FFN_WS_GHP, BL_FFN_WS_COUNT
+    BL_FFN_WS_GH, BL_FFN_WS_QH, BL_FFN_WS_RSH, BL_FFN_WS_GHP, BL_FFN_WS_PART, BL_FFN_WS_COUNT
 };
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t *off);
 size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F);

@@ -17,7 +17,7 @@ BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP = range(6)
 BL_TERNARY, BL_BINARY = 0, 1
 BL_F32, BL_BF16 = 0, 1
 BL_KERNEL_AUTO, BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_TILED = range(4)
-FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "GH", "QH", "RSH", "GHP")
+FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "GH", "QH", "RSH", "GHP", "PART")
 
 _lib = None
 

@@ -28,6 +28,41 @@ __device__ __forceinline__ uint4 load_stream_u4(const uint4* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+
+// Raw buffer resource over [base, base + nbytes): loads past nbytes return 0.
+__device__ __forceinline__ buf_rsrc make_buf_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+
+// LDS bytes stage_rows_lds writes for M rows of the given pitch.
+__host__ __device__ constexpr int64_t staged_rows_bytes(int64_t M, int64_t pitch) {
+  return (M * pitch + 1023) / 1024 * 1024;
+}
+
+// Copies bytes [k0, k0 + klen) of rows 0 .. M-1 of an int8 matrix (row stride
+// Kp) into LDS rows of `pitch` bytes (pitch >= klen, multiples of 16; the
+// bytes of a row past klen read as zero) with direct-to-LDS buffer loads:
+// each load moves 64 lanes x 16 bytes into 1 KB of LDS in lane order, so all
+// of the block's loads are in flight at once and no register holds the data.
+// dst spans staged_rows_bytes(M, pitch).  The data is in LDS once this
+// thread's loads have completed (s_waitcnt vmcnt(0)) and the block has
+// synchronised.  Requires M * Kp < 2^30.
+template <int NT>
+__device__ __forceinline__ void stage_rows_lds(const int8_t* X, int64_t Kp, int M, int64_t k0,
+                                               int klen, int pitch, int8_t* dst) {
+  const buf_rsrc r = make_buf_rsrc(X, (uint32_t)(M * Kp));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int units = (int)(staged_rows_bytes(M, pitch) / 1024);
+  for (int u = wave; u < units; u += NT / 64) {
+    const int o = 1024 * u + 16 * lane;
+    const int row = o / pitch, col = o - row * pitch;
+    const int voff = (row < M && col < klen) ? (int)(row * Kp + k0) + col : 0x40000000;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * u, 16, voff, 0, 0, 0);
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }

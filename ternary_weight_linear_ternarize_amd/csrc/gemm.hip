@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   const int g = lane >> 4, li = lane & 15;
   const int64_t pitch = Kp + 16;                 // staged activation row
   int8_t* lds_x = lds;
-  const int64_t xbytes = ((M * pitch + 15) / 16) * 16;
+  const int64_t xbytes = staged_rows_bytes(M, pitch);
   int8_t* lds_w = lds + xbytes + (int64_t)wave * NB * 16 * BP;
   v4i* lds_part = reinterpret_cast<v4i*>(lds + xbytes + (int64_t)WPB * NB * 16 * BP);
   const int64_t wpr = Kp / 16;
@@ -326,13 +326,9 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < nsteps) load_step(d, st[d]);
-  // activations -> LDS
-  const int64_t pieces = Kp / 16;
-  for (int64_t u = tid; u < (int64_t)M * pieces; u += 64 * WPB) {
-    const int64_t m = u / pieces, c = u - m * pieces;
-    *reinterpret_cast<uint4*>(lds_x + m * pitch + 16 * c) =
-        *reinterpret_cast<const uint4*>(Xq + m * Kp + 16 * c);
-  }
+  // activations -> LDS, every load in flight at once
+  stage_rows_lds<64 * WPB>(Xq, Kp, M, 0, (int)Kp, (int)pitch, lds_x);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   v4i acc[NB][2];
@@ -457,7 +453,7 @@ constexpr int kStreamLpr = 32;
 constexpr int kStreamBp = kStreamLpr * 16 + 16;  // staged bytes per weight row and step
 
 static int64_t stream_lds_bytes(int64_t M, int64_t Kp, int nb, int wpb, int ks) {
-  return (M * (Kp + 16) + 15) / 16 * 16 + (int64_t)wpb * nb * 16 * kStreamBp +
+  return staged_rows_bytes(M, Kp + 16) + (int64_t)wpb * nb * 16 * kStreamBp +
          (int64_t)(wpb / ks) * (ks - 1) * nb * 1024;
 }
 

@@ -5,14 +5,6 @@
 
 namespace bl {
 
-typedef __amdgpu_buffer_rsrc_t buf_rsrc;
-
-// Raw buffer resource over [base, base + nbytes): loads past nbytes return 0.
-__device__ __forceinline__ buf_rsrc make_buf_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
-                                           0x00020000);
-}
-
 // The four shifted-code byte vectors of one packed word (weights 16j + 4s + b
 // of the word sit in byte b of vector s).
 __device__ __forceinline__ v4i unpack_operand32(uint32_t w) {

@@ -240,7 +240,8 @@ def test_ffn_2b_bf16_random_norm(M):
     _ffn_case(M, True, "random")
 
 
-@pytest.mark.parametrize("M,D,F", [(1, 300, 700), (2, 64, 128), (2, 17000, 100), (17, 512, 1000), (100, 256, 520),
+@pytest.mark.parametrize("M,D,F", [(1, 300, 700), (2, 64, 128), (2, 17000, 100), (17, 512, 1000), (40, 1000, 3000),
+                                   (100, 256, 520),
                                    (256, 512, 1024)])
 def test_ffn_ragged_shapes(M, D, F):
     s = 500 + M
