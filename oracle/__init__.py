@@ -56,8 +56,8 @@ def _load():
     lib.orc_dequant.argtypes = [P, P, F, I64, I64, P]
     lib.orc_rmsnorm.argtypes = [P, P, F, I64, I64, P]
     lib.orc_relu2_mul.argtypes = [P, P, I64, P]
-    lib.orc_ffn.argtypes = [P, I64, I64, I64, P, F, P, F, P, F, P, F,
-                            P, P, P, P, P, P, P]
+    lib.orc_ffn.argtypes = [P, I64, I64, I64, P, F, P, F, P, F, P, F, ctypes.c_int, P, F,
+                            P, P, P, P, P, P, P, P]
     lib.orc_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -195,16 +195,20 @@ def bitlinear(x, t, gamma_w):
     return {"q": q, "gamma_x": gx, "rowsum": rs, "acc": acc, "y": y}
 
 
-def ffn(x, norm_w, norm_eps, tg, sg, tu, su, td, sd):
-    """RMSNorm -> quant -> gate/up -> relu(gate)^2*up -> requant -> down."""
+def ffn(x, norm_w, norm_eps, tg, sg, tu, su, td, sd, subln=False, subln_w=None,
+        subln_eps=float(np.finfo(np.float32).eps)):
+    """RMSNorm -> quant -> gate/up -> relu(gate)^2*up -> [RMSNorm if subln] ->
+    requant -> down."""
     x = _f32(x)
     M, D = x.shape
     F = tg.shape[0]
     assert tg.shape == (F, D) and tu.shape == (F, D) and td.shape == (D, F)
     nw = _f32(norm_w) if norm_w is not None else None
+    sw = _f32(subln_w) if subln_w is not None else None
     out = {
         "xn": np.empty((M, D), np.float32), "qx": np.empty((M, D), np.int8),
         "gx": np.empty(M, np.float32), "h": np.empty((M, F), np.float32),
+        "hn": np.empty((M, F), np.float32),
         "qh": np.empty((M, F), np.int8), "gh": np.empty(M, np.float32),
         "y": np.empty((M, D), np.float32),
     }
@@ -213,8 +217,11 @@ def ffn(x, norm_w, norm_eps, tg, sg, tu, su, td, sd):
     _load().orc_ffn(_ptr(x), M, D, F, _ptr(nw), float(np.float32(norm_eps)),
                     _ptr(tg), float(np.float32(sg)), _ptr(tu), float(np.float32(su)),
                     _ptr(td), float(np.float32(sd)),
+                    1 if subln else 0, _ptr(sw), float(np.float32(subln_eps)),
                     _ptr(out["xn"]), _ptr(out["qx"]), _ptr(out["gx"]), _ptr(out["h"]),
-                    _ptr(out["qh"]), _ptr(out["gh"]), _ptr(out["y"]))
+                    _ptr(out["hn"]), _ptr(out["qh"]), _ptr(out["gh"]), _ptr(out["y"]))
+    if not subln:
+        del out["hn"]
     return out
 
 

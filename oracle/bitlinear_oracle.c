@@ -282,13 +282,19 @@ void orc_bitlinear(const float *x, int64_t M, int64_t K, const int8_t *t, float 
 
 /* The feed-forward block: RMSNorm(D) -> int8 quant -> gate and up BitLinears
  * (D -> F) -> relu(gate)^2 * up -> int8 requant -> down BitLinear (F -> D).
- * Internal tensors are returned for inspection; any of them may be NULL
- * except the ones needed as scratch, which the caller provides:
- *   xn [M][D], qx [M][D], gx [M], hx [M][F], qh [M][F], gh [M], y [M][D]. */
+ * With subln != 0 the down BitLinear normalises its input first, as every
+ * BitLinear of [P1] "BitNet b1.58" does (self.norm before the activation
+ * quantiser; the sub-layer norm of [P4] "正規化で分散を安定させる" and [P5]):
+ * hn = RMSNorm(h) over F with weight subln_w (NULL: ones) and subln_eps, and
+ * the requantisation reads hn instead of h.
+ * Internal tensors are returned for inspection; the caller provides
+ *   xn [M][D], qx [M][D], gx [M], hx [M][F], hn [M][F] (used only with
+ *   subln), qh [M][F], gh [M], y [M][D]. */
 void orc_ffn(const float *x, int64_t M, int64_t D, int64_t F, const float *norm_w,
              float norm_eps, const int8_t *tg, float sg, const int8_t *tu, float su,
-             const int8_t *td, float sd, float *xn, int8_t *qx, float *gx, float *hx,
-             int8_t *qh, float *gh, float *y) {
+             const int8_t *td, float sd, int subln, const float *subln_w, float subln_eps,
+             float *xn, int8_t *qx, float *gx, float *hx, float *hn, int8_t *qh, float *gh,
+             float *y) {
     orc_rmsnorm(x, norm_w, norm_eps, M, D, xn);
     orc_act_quant(xn, M, D, qx, gx, NULL);
     int32_t *acc_g = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * F));
@@ -301,7 +307,12 @@ void orc_ffn(const float *x, int64_t M, int64_t D, int64_t F, const float *norm_
     orc_dequant(acc_g, gx, sg, M, F, yg);
     orc_dequant(acc_u, gx, su, M, F, yu);
     orc_relu2_mul(yg, yu, M * F, hx);
-    orc_act_quant(hx, M, F, qh, gh, NULL);
+    if (subln) {
+        orc_rmsnorm(hx, subln_w, subln_eps, M, F, hn);
+        orc_act_quant(hn, M, F, qh, gh, NULL);
+    } else {
+        orc_act_quant(hx, M, F, qh, gh, NULL);
+    }
     orc_int_linear(qh, td, M, D, F, acc_d);
     orc_dequant(acc_d, gh, sd, M, D, y);
     free(acc_g);

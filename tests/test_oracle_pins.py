@@ -422,6 +422,82 @@ def test_ffn_zero_cases():
 
 
 # ----------------------------------------------------------------------------
+# SubLN variant of the FFN: RMSNorm of h (over F) before the down quantiser
+
+def _constant_h_ffn(sign, su):
+    """Gate and up rows all +1 (up rows all `sign`) against non-negative
+    inputs: g > 0 and u constant along F, so each hidden row is constant."""
+    M, D, F = 3, 128, 192
+    x = np.abs(synth.normal(21, 1, (M, D)))
+    tg = np.ones((F, D), np.int8)
+    tu = np.full((F, D), sign, np.int8)
+    sd, td, _ = oracle.quantize_weights(synth.normal(21, 4, (D, F), 0.02))
+    return x, tg, tu, td, sd, su
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_subln_maps_constant_rows_to_full_scale_codes(sign):
+    """RMSNorm (eps 0) of a constant row c is c / sqrt(c^2) = sign(c) up to two
+    roundings, so every code of the requantised row is sign(c) * 127, however
+    small |c| is; the plain block (no norm) quantises a row with |c| near the
+    quantiser's 1e-5 offset to codes near 127 |c| / (|c| + 1e-5)."""
+    x, tg, tu, td, sd, su = _constant_h_ffn(sign, np.float32(1e-10))
+    out = oracle.ffn(x, None, 0.0, tg, np.float32(0.02), tu, su, td, sd, subln=True, subln_eps=0.0)
+    h = out["h"]
+    assert (h == h[:, :1]).all() and (np.sign(h) == sign).all()
+    assert (np.abs(h) < 1e-4).all()
+    assert (out["qh"] == sign * 127).all()
+    np.testing.assert_allclose(out["hn"], sign, rtol=2 ** -22)
+    # the integer down projection of a full-scale row: 127 * sign * row sums of t_d
+    acc = 127 * sign * td.astype(np.int64).sum(1)
+    np.testing.assert_array_equal(out["y"], oracle.dequant(np.tile(acc, (3, 1)), out["gh"], sd))
+    plain = oracle.ffn(x, None, 0.0, tg, np.float32(0.02), tu, su, td, sd)
+    c = np.abs(plain["h"][:, 0]).astype(np.float64)
+    np.testing.assert_array_equal(np.abs(plain["qh"][:, 0]), np.rint(127 * c / (c + 1e-5)))
+    assert (np.abs(plain["qh"]) < 127).all()
+
+
+def test_subln_output_is_invariant_to_powers_of_two_in_h():
+    """Scaling the up weights' scale by 2^k scales h by exactly 2^k; with
+    eps 0 the mean square scales by 4^k and its square root by 2^k with no
+    new rounding, so hn, the codes and y do not change by a single bit."""
+    x, ((sg, tg, _), (su, tu, _), (sd, td, _)) = _small_ffn(17)
+    sw = (np.float32(1) + synth.normal(17, 9, (tg.shape[0],), 0.1)).astype(np.float32)
+    eps = float(np.finfo(np.float32).eps)
+    base = oracle.ffn(x, None, eps, tg, sg, tu, su, td, sd, subln=True, subln_w=sw, subln_eps=0.0)
+    assert (np.abs(base["h"]).max(axis=1) > 0).all()  # no 0/0 with eps 0
+    for k in (-6, -1, 3, 9):
+        o = oracle.ffn(x, None, eps, tg, sg, tu, np.float32(su * np.float32(2.0 ** k)), td, sd,
+                       subln=True, subln_w=sw, subln_eps=0.0)
+        np.testing.assert_array_equal(o["h"], base["h"] * np.float32(2.0 ** k))
+        np.testing.assert_array_equal(o["hn"], base["hn"])
+        np.testing.assert_array_equal(o["qh"], base["qh"])
+        np.testing.assert_array_equal(o["y"], base["y"])
+
+
+def test_subln_weight_scales_each_channel():
+    """hn = (h * r) * w_j: with per-channel powers of two as weights every
+    column of hn is the unit-weight column times its own w_j, exactly."""
+    x, ((sg, tg, _), (su, tu, _), (sd, td, _)) = _small_ffn(19)
+    F = tg.shape[0]
+    eps = float(np.finfo(np.float32).eps)
+    ones = oracle.ffn(x, None, eps, tg, sg, tu, su, td, sd, subln=True)
+    p2 = np.exp2(np.arange(F) % 7 - 3).astype(np.float32)
+    o = oracle.ffn(x, None, eps, tg, sg, tu, su, td, sd, subln=True, subln_w=p2)
+    np.testing.assert_array_equal(o["hn"], ones["hn"] * p2[None, :])
+    np.testing.assert_array_equal(o["h"], ones["h"])
+
+
+def test_subln_off_leaves_the_block_unchanged():
+    x, ((sg, tg, _), (su, tu, _), (sd, td, _)) = _small_ffn(18)
+    eps = float(np.finfo(np.float32).eps)
+    a = oracle.ffn(x, None, eps, tg, sg, tu, su, td, sd)
+    b = oracle.ffn(x, None, eps, tg, sg, tu, su, td, sd, subln=False, subln_w=np.ones(tg.shape[0], np.float32))
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+# ----------------------------------------------------------------------------
 # end-to-end on the single-layer workload (512 -> 400, 16 tokens)
 
 def test_single_layer_end_to_end_against_float_reference():
