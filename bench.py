@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "ffn", "copy"],
                     help="run one workload's kernels eagerly --steps times and exit "
                          "(for profilers); prints a short JSON line")
+    ap.add_argument("--subln", action="store_true",
+                    help="with --only ffn: the SubLN variant of the block")
     return ap.parse_args()
 
 
@@ -125,10 +127,11 @@ def only_workload(args):
             H = torch.from_numpy(f["H"][:M]).to(dev)
             ws = torch.empty(B.lib().bitnet_ffn_workspace_bytes(M, D, F), dtype=torch.uint8, device=dev)
             Y = torch.empty((M, D), dtype=torch.float32, device=dev)
+            sw = torch.from_numpy(f["subln_w"]).to(dev) if args.subln else None
             for i in range(n):
                 g, u, dn = cps[i % ncp]
                 B.bitnet_ffn_forward(H, None, eps, g[0], g[1], u[0], u[1], dn[0], dn[1], D, F,
-                                     out=Y, ws=ws)
+                                     out=Y, ws=ws, subln_w=sw, subln_eps=eps)
     torch.cuda.synchronize()
     return {"only": args.only, "launches_per_shape": n}
 
@@ -377,20 +380,21 @@ def extra_workloads(torch, B, synth, dev):
     ncp = max(2, int(np.ceil(600e6 / wbytes)))
     cps = [[(pk[0].clone(), pk[1]) for pk in packs] for _ in range(ncp)]
     eps = float(np.finfo(np.float32).eps)
+    subln_w = torch.from_numpy(f["subln_w"]).to(dev)
     for M in c["M_list"]:
         H = torch.from_numpy(f["H"][:M]).to(dev)
         ws = torch.empty(B.lib().bitnet_ffn_workspace_bytes(M, D, F), dtype=torch.uint8, device=dev)
         Y = torch.empty((M, D), dtype=torch.float32, device=dev)
+        for tag, sw in (("", None), ("_subln", subln_w)):
+            def run(i):
+                g, u, dn = cps[i % ncp]
+                B.bitnet_ffn_forward(H, None, eps, g[0], g[1], u[0], u[1], dn[0], dn[1], D, F,
+                                     out=Y, ws=ws, subln_w=sw, subln_eps=eps)
 
-        def run(i):
-            g, u, dn = cps[i % ncp]
-            B.bitnet_ffn_forward(H, None, eps, g[0], g[1], u[0], u[1], dn[0], dn[1], D, F,
-                                 out=Y, ws=ws)
-
-        ms = graph_time_per_launch(run, ncp, 5, torch)
-        res[f"ffn_2b_M{M}"] = {"avg_us": round(ms * 1e3, 2),
-                               "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
-                               "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            ms = graph_time_per_launch(run, ncp, 5, torch)
+            res[f"ffn_2b{tag}_M{M}"] = {"avg_us": round(ms * 1e3, 2),
+                                        "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                                        "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del cps, packs
     torch.cuda.empty_cache()
     return res

@@ -185,13 +185,14 @@ int bitlinear_forward_fused(const void *X, int dtype, int64_t M, int64_t K, cons
  *   XN  float [M][D]   RMSNorm output
  *   QX  int8  [M][Dp]  its int8 codes;   GX float [M] scales;  RSX int32 [M] row sums
  *   H   float [M][F]   relu(gate)^2 * up
+ *   HN  float [M][F]   RMSNorm(h) (written only with SubLN)
  *   GH  float [M]      max |h| per token (stored as float bits)
  *   QH  int8  [M][Fp]  int8 codes of h;  RSH int32 [M] row sums
  *   GHP float [P][M]   per-block partial maxima of |h| (scratch)
  *   PART int32         split-K partial sums of the down projection for
  *                      17..64 tokens (scratch; size 0 otherwise)           */
 enum {
-    BL_FFN_WS_XN = 0, BL_FFN_WS_QX, BL_FFN_WS_GX, BL_FFN_WS_RSX, BL_FFN_WS_H,
+    BL_FFN_WS_XN = 0, BL_FFN_WS_QX, BL_FFN_WS_GX, BL_FFN_WS_RSX, BL_FFN_WS_H, BL_FFN_WS_HN,
     BL_FFN_WS_GH, BL_FFN_WS_QH, BL_FFN_WS_RSH, BL_FFN_WS_GHP, BL_FFN_WS_PART, BL_FFN_WS_COUNT
 };
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t *off);
@@ -202,13 +203,18 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F);
  *   xn = RMSNorm(H) ([P1] "BitNet b1.58": normalise before quantising);
  *   g  = BitLinear_gate(xn), u = BitLinear_up(xn)   (D -> F, shared quant);
  *   h  = relu(g)^2 * u                               ([P5] ReLU², gated);
- *   Y  = BitLinear_down(h)                            (F -> D, h requantised).
+ *   hn = RMSNorm(h) over F, only with SubLN (subln_w != NULL): the norm
+ *        every BitLinear of [P1] "BitNet b1.58" applies before quantising,
+ *        the sub-layer norm of [P4] "正規化で分散を安定させる" and [P5];
+ *   Y  = BitLinear_down(hn or h)                      (F -> D, requantised).
  * RMSNorm: ms = binary32(binary64(exact sum x^2) / D); r = 1 / sqrt(ms + eps);
  * xn = (x * r) * norm_w.  No residual is added (the caller owns it).
  *
  *  H        [M][D] float32 or bfloat16 (dtype), device.
  *  norm_w   [D] float, device, or NULL for ones.  norm_eps: RMSNorm epsilon
  *           (PyTorch's default for float32 is 2^-23).
+ *  subln_w  [F] float, device: SubLN weight; NULL = no SubLN (the block as
+ *           the 2B-class FFN workload states it).  subln_eps: its epsilon.
  *  Wg, Wu   [F][Dp/16] packed (16-byte aligned), sg, su their scales.
  *  Wd       [D][Fp/16] packed, sd its scale.
  *  Y        [M][D] float32, device, written.
@@ -216,7 +222,8 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F);
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP.
  */
 int bitnet_ffn_forward(const void *H, int dtype, int64_t M, int64_t D, int64_t F,
-                       const float *norm_w, float norm_eps, const uint32_t *Wg,
+                       const float *norm_w, float norm_eps, const float *subln_w,
+                       float subln_eps, const uint32_t *Wg,
                        const float *sg, const uint32_t *Wu, const float *su,
                        const uint32_t *Wd, const float *sd, float *Y, void *ws,
                        size_t ws_bytes, void *stream);

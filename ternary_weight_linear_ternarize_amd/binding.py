@@ -17,7 +17,7 @@ BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP = range(6)
 BL_TERNARY, BL_BINARY = 0, 1
 BL_F32, BL_BF16 = 0, 1
 BL_KERNEL_AUTO, BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_TILED = range(4)
-FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "GH", "QH", "RSH", "GHP", "PART")
+FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "HN", "GH", "QH", "RSH", "GHP", "PART")
 
 _lib = None
 
@@ -65,7 +65,8 @@ def lib():
     L.bitnet_ffn_workspace_layout.restype = SZ
     L.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
     L.bitnet_ffn_workspace_bytes.restype = SZ
-    L.bitnet_ffn_forward.argtypes = [P, I, I64, I64, I64, P, F, P, P, P, P, P, P, P, P, SZ, P]
+    L.bitnet_ffn_forward.argtypes = [P, I, I64, I64, I64, P, F, P, F, P, P, P, P, P, P, P, P, SZ,
+                                     P]
     L.bitnet_ffn_forward.restype = I
     _lib = L
     return L
@@ -201,8 +202,11 @@ def fused_internals(ws, M, K):
             "x_rowsum": ws[o2:o2 + 4 * M].view(torch.int32)}
 
 
-def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=None, ws=None):
-    """FFN block; returns (Y [M, D] float32, workspace uint8 tensor)."""
+def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=None, ws=None,
+                       subln_w=None, subln_eps=2.0 ** -23):
+    """FFN block; returns (Y [M, D] float32, workspace uint8 tensor).  With
+    subln_w (a [F] float32 tensor) h is RMS-normalised before the down
+    projection's quantiser."""
     M = H.shape[0]
     if H.dtype == torch.float32:
         dt = BL_F32
@@ -216,7 +220,7 @@ def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=No
     ws = ws if ws is not None else torch.empty(nws, dtype=torch.uint8, device=dev)
     st = lib().bitnet_ffn_forward(
         _dev(H, "H"), dt, M, D, F, _opt(norm_w, "norm_w"), float(norm_eps),
-        _dev(Wg, "Wg"), _dev(sg, "sg"), _dev(Wu, "Wu"), _dev(su, "su"),
+        _opt(subln_w, "subln_w"), float(subln_eps), _dev(Wg, "Wg"), _dev(sg, "sg"), _dev(Wu, "Wu"), _dev(su, "su"),
         _dev(Wd, "Wd"), _dev(sd, "sd"), _dev(Y, "Y"), _dev(ws, "ws"), ws.numel(), _stream(dev))
     _check(st, "bitnet_ffn_forward")
     return Y, ws
@@ -237,6 +241,7 @@ def ffn_internals(ws, M, D, F):
         "gx": view("GX", torch.float32, M, (M,)),
         "rsx": view("RSX", torch.int32, M, (M,)),
         "h": view("H", torch.float32, M * F, (M, F)),
+        "hn": view("HN", torch.float32, M * F, (M, F)),
         "gh": view("GH", torch.float32, M, (M,)),
         "qh": view("QH", torch.int8, M * fp, (M, fp)),
         "rsh": view("RSH", torch.int32, M, (M,)),

@@ -172,6 +172,7 @@ size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off)
       m * 4,                   // GX
       m * 4,                   // RSX
       m * (size_t)F * 4,       // H
+      m * (size_t)F * 4,       // HN
       m * 4,                   // GH
       m * (size_t)padk(F),     // QH
       m * 4,                   // RSH
@@ -191,7 +192,8 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F) {
 }
 
 int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
-                       const float* norm_w, float norm_eps, const uint32_t* Wg, const float* sg,
+                       const float* norm_w, float norm_eps, const float* subln_w,
+                       float subln_eps, const uint32_t* Wg, const float* sg,
                        const uint32_t* Wu, const float* su, const uint32_t* Wd, const float* sd,
                        float* Y, void* ws, size_t ws_bytes, void* stream) {
   if (!H || !Wg || !sg || !Wu || !su || !Wd || !sd || !Y) return BL_EINVAL;
@@ -202,7 +204,8 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   if (!ws || ws_bytes < need) return BL_EWORKSPACE;
   if (!aligned(H, dtype == BL_F32 ? 4 : 2) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
       !aligned(Wd, 16) || !aligned(Y, 4) || !aligned(ws, 256) || !aligned(sg, 4) ||
-      !aligned(su, 4) || !aligned(sd, 4) || (norm_w && !aligned(norm_w, 4)))
+      !aligned(su, 4) || !aligned(sd, 4) || (norm_w && !aligned(norm_w, 4)) ||
+      (subln_w && !aligned(subln_w, 4)))
     return BL_EALIGN;
   char* base = reinterpret_cast<char*>(ws);
   float* xn = reinterpret_cast<float*>(base + off[BL_FFN_WS_XN]);
@@ -210,6 +213,7 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   float* gx = reinterpret_cast<float*>(base + off[BL_FFN_WS_GX]);
   int32_t* rsx = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_RSX]);
   float* h = reinterpret_cast<float*>(base + off[BL_FFN_WS_H]);
+  float* hn = reinterpret_cast<float*>(base + off[BL_FFN_WS_HN]);
   float* gh = reinterpret_cast<float*>(base + off[BL_FFN_WS_GH]);
   int8_t* qh = reinterpret_cast<int8_t*>(base + off[BL_FFN_WS_QH]);
   int32_t* rsh = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_RSH]);
@@ -227,12 +231,16 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   else
     e = bl::launch_mfma_gateup(qx, gx, rsx, M, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
   if (e != hipSuccess) return BL_EHIP;
-  if (M == 1 && bl::gemv_fused_ok(F)) {
+  if (subln_w) {
+    // SubLN: RMSNorm of h, then its int8 codes
+    e = bl::launch_rmsnorm_quant(h, false, M, F, subln_w, subln_eps, hn, qh, gh, rsh, s);
+  } else if (M == 1 && bl::gemv_fused_ok(F)) {
     // requantise h inside the down GEMV (scale from the partial maxima)
     e = bl::launch_gemv_parts(h, ghp, nparts, F, Wd, sd, D, Y, qh, gh, rsh, s);
     return hip_status(e);
+  } else {
+    e = bl::launch_act_quant(h, false, M, F, qh, gh, rsh, ghp, nparts, s);
   }
-  e = bl::launch_act_quant(h, false, M, F, qh, gh, rsh, ghp, nparts, s);
   if (e != hipSuccess) return BL_EHIP;
   if (M == 1)
     e = bl::launch_gemv(qh, gh, rsh, F, Wd, sd, D, Y, nullptr, s);

@@ -21,7 +21,7 @@ FFN_2B = dict(M_list=(1, 8, 64), D=2560, F=6912, seed=3)
 DECODE_100B = dict(M_list=(1, 8), K=8192, N=28672, seed=4)
 
 # tensor ids inside a workload seed
-T_W, T_X, T_W2, T_X2, T_W3, T_NORM, T_OUTLIER = range(7)
+T_W, T_X, T_W2, T_X2, T_W3, T_NORM, T_OUTLIER, T_SUBLN = range(8)
 
 
 def _gen(seed, tensor_id):
@@ -85,6 +85,8 @@ def ffn_2b(norm="ones"):
         out["norm_w"] = np.ones(D, dtype=np.float32)
     else:
         out["norm_w"] = (np.float32(1.0) + normal(s, T_NORM, (D,), 0.1)).astype(np.float32)
+    # SubLN weight over F (used only by the SubLN variant of the block)
+    out["subln_w"] = (np.float32(1.0) + normal(s, T_SUBLN, (F,), 0.1)).astype(np.float32)
     return out
 
 

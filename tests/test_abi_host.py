@@ -102,18 +102,21 @@ def test_ffn_validation():
     lib = B.lib()
     M, D, F = 2, 64, 128
     n = lib.bitnet_ffn_workspace_bytes(M, D, F)
-    base = [FAKE, 0, M, D, F, None, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n, None]
+    base = [FAKE, 0, M, D, F, None, 1e-6, None, 1e-6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, n, None]
     a = list(base); a[0] = None
     assert lib.bitnet_ffn_forward(*a) == B.BL_EINVAL
     a = list(base); a[1] = 5
     assert lib.bitnet_ffn_forward(*a) == B.BL_EINVAL
     a = list(base); a[4] = 0
     assert lib.bitnet_ffn_forward(*a) == B.BL_ESHAPE
-    a = list(base); a[15] = n - 1
+    a = list(base); a[17] = n - 1
     assert lib.bitnet_ffn_forward(*a) == B.BL_EWORKSPACE
-    a = list(base); a[14] = ctypes.c_void_p(0x10010)  # 16 B aligned, not 256
+    a = list(base); a[16] = ctypes.c_void_p(0x10010)  # 16 B aligned, not 256
     assert lib.bitnet_ffn_forward(*a) == B.BL_EALIGN
-    a = list(base); a[7] = ODD
+    a = list(base); a[9] = ODD
+    assert lib.bitnet_ffn_forward(*a) == B.BL_EALIGN
+    a = list(base); a[7] = ODD  # SubLN weight
     assert lib.bitnet_ffn_forward(*a) == B.BL_EALIGN
 
 

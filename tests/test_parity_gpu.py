@@ -198,7 +198,7 @@ def test_decode_100b_full(mode):
         check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(M)[:3])
 
 
-def _ffn_case(M, bf16, norm):
+def _ffn_case(M, bf16, norm, subln=False):
     d = synth.ffn_2b(norm=norm)
     D, F = synth.FFN_2B["D"], synth.FFN_2B["F"]
     pk = {}
@@ -211,11 +211,16 @@ def _ffn_case(M, bf16, norm):
         H = Hd.float().cpu().numpy()
     nw = d["norm_w"]
     eps = float(np.finfo(np.float32).eps)
+    sw = d["subln_w"] if subln else None
     ref = oracle.ffn(H, nw, eps, pk["W_gate"][1], pk["W_gate"][0], pk["W_up"][1], pk["W_up"][0],
-                     pk["W_down"][1], pk["W_down"][0])
+                     pk["W_down"][1], pk["W_down"][0], subln=subln, subln_w=sw, subln_eps=eps)
+    kw = dict(subln_w=to_dev(sw), subln_eps=eps) if subln else {}
     Y, ws = B.bitnet_ffn_forward(Hd, to_dev(nw), eps, pk["W_gate"][2], pk["W_gate"][3],
-                                 pk["W_up"][2], pk["W_up"][3], pk["W_down"][2], pk["W_down"][3], D, F)
+                                 pk["W_up"][2], pk["W_up"][3], pk["W_down"][2], pk["W_down"][3], D, F,
+                                 **kw)
     it = {k: host(v) for k, v in B.ffn_internals(ws, M, D, F).items()}
+    if subln:
+        np.testing.assert_array_equal(it["hn"].view(np.uint32), ref["hn"].view(np.uint32))
     np.testing.assert_array_equal(it["xn"].view(np.uint32), ref["xn"].view(np.uint32))
     np.testing.assert_array_equal(it["qx"][:, :D], ref["qx"])
     np.testing.assert_array_equal(it["gx"].view(np.uint32), ref["gx"].view(np.uint32))
@@ -226,7 +231,8 @@ def _ffn_case(M, bf16, norm):
     np.testing.assert_array_equal(it["rsh"], ref["qh"].astype(np.int64).sum(1))
     assert_rel(host(Y), ref["y"])
     Y2, _ = B.bitnet_ffn_forward(Hd, to_dev(nw), eps, pk["W_gate"][2], pk["W_gate"][3],
-                                 pk["W_up"][2], pk["W_up"][3], pk["W_down"][2], pk["W_down"][3], D, F)
+                                 pk["W_up"][2], pk["W_up"][3], pk["W_down"][2], pk["W_down"][3], D, F,
+                                 **kw)
     np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
 
 
@@ -240,23 +246,35 @@ def test_ffn_2b_bf16_random_norm(M):
     _ffn_case(M, True, "random")
 
 
-@pytest.mark.parametrize("M,D,F", [(1, 300, 700), (2, 64, 128), (2, 17000, 100), (17, 512, 1000), (40, 1000, 3000),
-                                   (100, 256, 520),
-                                   (256, 512, 1024)])
-def test_ffn_ragged_shapes(M, D, F):
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_ffn_2b_subln(M):
+    _ffn_case(M, M == 8, "random", subln=True)
+
+
+@pytest.mark.parametrize("M,D,F,subln", [(1, 300, 700, False), (2, 64, 128, False), (2, 17000, 100, False),
+                                         (17, 512, 1000, False), (40, 1000, 3000, False),
+                                         (100, 256, 520, False), (256, 512, 1024, False),
+                                         (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
+                                         (100, 256, 520, True)])
+def test_ffn_ragged_shapes(M, D, F, subln):
     s = 500 + M
     x = synth.normal(s, 1, (M, D))
     ws = [synth.normal(s, 2 + i, shp, 0.02) for i, shp in enumerate(((F, D), (F, D), (D, F)))]
     q = [oracle.quantize_weights(w) for w in ws]
     nw = (np.float32(1) + synth.normal(s, 9, (D,), 0.1)).astype(np.float32)
+    sw = (np.float32(1) + synth.normal(s, 10, (F,), 0.1)).astype(np.float32) if subln else None
     eps = 1e-6
-    ref = oracle.ffn(x, nw, eps, q[0][1], q[0][0], q[1][1], q[1][0], q[2][1], q[2][0])
+    ref = oracle.ffn(x, nw, eps, q[0][1], q[0][0], q[1][1], q[1][0], q[2][1], q[2][0],
+                     subln=subln, subln_w=sw, subln_eps=1e-5)
     pk = [B.bitlinear_pack(to_dev(w)) for w in ws]
     for i in range(3):
         np.testing.assert_array_equal(host(pk[i][0]).view(np.uint32), q[i][2])
+    kw = dict(subln_w=to_dev(sw), subln_eps=1e-5) if subln else {}
     Y, wsp = B.bitnet_ffn_forward(to_dev(x), to_dev(nw), eps, pk[0][0], pk[0][1], pk[1][0],
-                                  pk[1][1], pk[2][0], pk[2][1], D, F)
+                                  pk[1][1], pk[2][0], pk[2][1], D, F, **kw)
     it = {k: host(v) for k, v in B.ffn_internals(wsp, M, D, F).items()}
+    if subln:
+        np.testing.assert_array_equal(it["hn"].view(np.uint32), ref["hn"].view(np.uint32))
     np.testing.assert_array_equal(it["xn"].view(np.uint32), ref["xn"].view(np.uint32))
     np.testing.assert_array_equal(it["qx"][:, :D], ref["qx"])
     np.testing.assert_array_equal(it["h"].view(np.uint32), ref["h"].view(np.uint32))
