@@ -51,6 +51,12 @@ def _load():
     lib.orc_pack.argtypes = [P, I64, I64, P]
     lib.orc_unpack.argtypes = [P, I64, I64, P]
     lib.orc_unpack.restype = I64
+    lib.orc_padded_k1.argtypes = [I64]
+    lib.orc_padded_k1.restype = I64
+    lib.orc_pack1.argtypes = [P, I64, I64, P]
+    lib.orc_pack1.restype = I64
+    lib.orc_unpack1.argtypes = [P, I64, I64, P]
+    lib.orc_unpack1.restype = I64
     lib.orc_act_quant.argtypes = [P, I64, I64, P, P, P]
     lib.orc_int_linear.argtypes = [P, P, I64, I64, I64, P]
     lib.orc_dequant.argtypes = [P, P, F, I64, I64, P]
@@ -125,6 +131,32 @@ def unpack(packed, K):
     assert packed.shape[1] == padded_k(K) // 16
     t = np.zeros((N, K), dtype=np.int8)
     bad = _load().orc_unpack(_ptr(packed), N, K, _ptr(t))
+    return t, int(bad)
+
+
+def padded_k1(K):
+    return int(_load().orc_padded_k1(int(K)))
+
+
+def pack1(t):
+    """Pack an int8 binary matrix [N, K] (values -1/+1) into the 1-bit layout,
+    uint32 words [N, padded_k1(K)//32].  Raises on other values."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    N, K = t.shape
+    out = np.empty((N, padded_k1(K) // 32), dtype=np.uint32)
+    bad = _load().orc_pack1(_ptr(t), N, K, _ptr(out))
+    if bad:
+        raise ValueError(f"pack1: {bad} values other than -1/+1")
+    return out
+
+
+def unpack1(packed, K):
+    """Inverse of pack1.  Returns (t [N, K] int8, number of set padding bits)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint32)
+    N = packed.shape[0]
+    assert packed.shape[1] == padded_k1(K) // 32
+    t = np.zeros((N, K), dtype=np.int8)
+    bad = _load().orc_unpack1(_ptr(packed), N, K, _ptr(t))
     return t, int(bad)
 
 

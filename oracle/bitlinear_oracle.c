@@ -193,6 +193,59 @@ int64_t orc_unpack(const uint32_t *packed, int64_t N, int64_t K, int8_t *t) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Packed 1-bit layout for the binary variant ([P1] "1-Bit重みとSign関数":
+ * W_b = Sign(W) has two values, so one bit per weight suffices; [P2] counts
+ * the 1-bit memory saving).  Layout of this build:
+ *   row n holds Kb = K rounded up to 128 weights as Kb/32 words;
+ *   word j covers weights 32j .. 32j+31;
+ *   weight 32j + 4s + b (s = 0..7, b = 0..3) is bit 8b + s of the word;
+ *   the bit is 1 for +1 and 0 for -1; weights k >= K are padding, bit 0. */
+int64_t orc_padded_k1(int64_t K) { return (K + 127) / 128 * 128; }
+
+/* t holds only -1 and +1; returns the number of other values met (packed
+ * as -1). */
+int64_t orc_pack1(const int8_t *t, int64_t N, int64_t K, uint32_t *packed) {
+    int64_t kb = orc_padded_k1(K);
+    int64_t words = kb / 32;
+    int64_t bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < words; ++j) {
+            uint32_t word = 0;
+            for (int64_t k = 32 * j; k < 32 * j + 32; ++k) {
+                uint32_t bit = 0u;
+                if (k < K) {
+                    int8_t v = t[n * K + k];
+                    if (v == 1) bit = 1u;
+                    else if (v != -1) ++bad;
+                }
+                int64_t r = k - 32 * j;
+                int64_t s = r / 4, b = r % 4;
+                word |= bit << (8 * b + s);
+            }
+            packed[n * words + j] = word;
+        }
+    }
+    return bad;
+}
+
+/* Inverse of orc_pack1.  Returns the number of padding bits that are set. */
+int64_t orc_unpack1(const uint32_t *packed, int64_t N, int64_t K, int8_t *t) {
+    int64_t kb = orc_padded_k1(K);
+    int64_t words = kb / 32;
+    int64_t bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < kb; ++k) {
+            int64_t j = k / 32, r = k % 32;
+            int64_t s = r / 4, b = r % 4;
+            uint32_t bit = (packed[n * words + j] >> (8 * b + s)) & 1u;
+            if (k < K) t[n * K + k] = bit ? (int8_t)1 : (int8_t)-1;
+            else if (bit) ++bad;
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------ */
 /* [P1] "BitNet b1.58" activation_quant: per token (row) scale = max |x| over
  * the row; x * Q / (scale + 1e-5), evaluated left to right, rounded half to
  * even, clamped.  Q = 127 and the clamp is [-127, 127] (symmetric range of

@@ -225,6 +225,71 @@ def test_unpack_rejects_code_11():
 
 
 # ----------------------------------------------------------------------------
+# 1-bit layout of the binary variant
+
+def test_pack1_matches_hand_worked_example():
+    g = _read_golden("binary_1bit_layout_example.txt")
+    K = int(g["K"][0])
+    t = np.array([int(v) for v in g["t"]], np.int8).reshape(1, K)
+    words = np.array([int(v, 16) for v in g["words"]], np.uint32)
+    np.testing.assert_array_equal(oracle.pack1(t)[0], words)
+    back, bad = oracle.unpack1(words.reshape(1, -1), K)
+    assert bad == 0
+    np.testing.assert_array_equal(back, t)
+
+
+def test_pack1_roundtrip_padding_and_two_bit_codes():
+    rng = np.random.default_rng(8)
+    for N, K in ((1, 1), (3, 31), (5, 32), (2, 64), (7, 127), (2, 128), (9, 129), (4, 1040), (40, 8192)):
+        t = (2 * rng.integers(0, 2, size=(N, K)) - 1).astype(np.int8)
+        p = oracle.pack1(t)
+        kb = oracle.padded_k1(K)
+        assert kb % 128 == 0 and kb - 128 < K <= kb
+        assert p.shape == (N, kb // 32)
+        back, bad = oracle.unpack1(p, K)
+        assert bad == 0
+        np.testing.assert_array_equal(back, t)
+        # bit k of the row, read straight from the layout rule
+        bits = np.zeros((N, kb), np.int64)
+        for k in range(kb):
+            j, r = divmod(k, 32)
+            s, b = divmod(r, 4)
+            bits[:, k] = (p[:, j] >> np.uint32(8 * b + s)) & 1
+        assert not bits[:, K:].any()
+        np.testing.assert_array_equal(2 * bits[:, :K] - 1, t)
+        # the 2-bit code of a binary weight is twice its bit
+        p2 = oracle.pack(t)
+        for k in range(0, K, max(1, K // 97)):
+            j, r = divmod(k, 16)
+            s, b = divmod(r, 4)
+            np.testing.assert_array_equal((p2[:, j] >> np.uint32(8 * b + 2 * s)) & 3, 2 * bits[:, k])
+
+
+def test_pack1_rejects_non_binary_values():
+    with pytest.raises(ValueError):
+        oracle.pack1(np.array([[1, 0, -1]], np.int8))
+
+
+def test_one_bit_product_identity_brute_force():
+    """acc = sum q t = 2 sum_{bit=1} q - sum q, read bit by bit from the words."""
+    rng = np.random.default_rng(9)
+    M, N, K = 3, 5, 200
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    t = (2 * rng.integers(0, 2, size=(N, K)) - 1).astype(np.int8)
+    p = oracle.pack1(t)
+    acc = oracle.int_linear(q, t)
+    for m in range(M):
+        for n in range(N):
+            pos = 0
+            for k in range(K):
+                j, r = divmod(k, 32)
+                s, b = divmod(r, 4)
+                if (int(p[n, j]) >> (8 * b + s)) & 1:
+                    pos += int(q[m, k])
+            assert acc[m, n] == 2 * pos - int(q[m].astype(np.int64).sum())
+
+
+# ----------------------------------------------------------------------------
 # a4: per-token absmax int8 activation quant
 
 def test_act_quant_matches_page_listing_in_torch():
