@@ -52,7 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "ffn", "copy"],
+    ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "decode100b_1bit", "ffn",
+                                       "copy"],
                     help="run one workload's kernels eagerly --steps times and exit "
                          "(for profilers); prints a short JSON line")
     ap.add_argument("--subln", action="store_true",
@@ -114,6 +115,19 @@ def only_workload(args):
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             for i in range(n):
                 B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y)
+    elif args.only == "decode100b_1bit":
+        c = synth.DECODE_100B
+        K, N = c["K"], c["N"]
+        p = synth.decode_100b()
+        Wb, sc = B.bitlinear_pack(torch.from_numpy(p["W"]).to(dev), B.BL_BINARY_1BIT)
+        del p["W"]
+        ncp = max(2, int(np.ceil(600e6 / (Wb.numel() * 4))))
+        cps = [Wb.clone() for _ in range(ncp)]
+        for M in (1, 8):
+            q = B.bitlinear_quant_act(torch.from_numpy(p["X"][:M]).to(dev))
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            for i in range(n):
+                B.bitlinear_forward_1bit(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y)
     elif args.only == "ffn":
         c = synth.FFN_2B
         D, F = c["D"], c["F"]
@@ -368,6 +382,23 @@ def extra_workloads(torch, B, synth, dev):
                     "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del cps, Wp
         torch.cuda.empty_cache()
+    # binary weights in the 1-bit layout (half the bytes of the 2-bit codes)
+    Wb, sc = B.bitlinear_pack(Wd, B.BL_BINARY_1BIT)
+    pb = Wb.numel() * 4
+    ncp = max(2, int(np.ceil(600e6 / pb)))
+    cps = [Wb.clone() for _ in range(ncp)]
+    for M in (1, 8):
+        q = B.bitlinear_quant_act(torch.from_numpy(p["X"][:M]).to(dev))
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ms = graph_time_per_launch(
+            lambda i: B.bitlinear_forward_1bit(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y),
+            ncp, 5, torch)
+        alg = pb + M * (K + 8) + 4 + M * N * 4
+        res[f"decode_100b_binary_1bit_M{M}"] = {
+            "avg_us": round(ms * 1e3, 2), "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del cps, Wb
+    torch.cuda.empty_cache()
     del Wd
     torch.cuda.empty_cache()
 

@@ -61,8 +61,9 @@ enum {
     BL_EHIP = 5        /* the HIP runtime reported an error when enqueuing the kernels */
 };
 
-/* Weight quantiser ([P1] "Absmean量子化関数" / "1-Bit重みとSign関数"). */
-enum { BL_TERNARY = 0, BL_BINARY = 1 };
+/* Weight quantiser ([P1] "Absmean量子化関数" / "1-Bit重みとSign関数").
+ * BL_BINARY_1BIT: the binary quantiser packed one bit per weight. */
+enum { BL_TERNARY = 0, BL_BINARY = 1, BL_BINARY_1BIT = 2 };
 
 /* Element type of float activations / hidden states (bf16 is widened exactly). */
 enum { BL_F32 = 0, BL_BF16 = 1 };
@@ -78,6 +79,13 @@ int64_t bl_padded_k(int64_t K);
 /* Bytes of a packed weight matrix: N * Kp / 4.  0 for invalid sizes. */
 size_t bl_packed_bytes(int64_t N, int64_t K);
 
+/* Kb: K rounded up to a multiple of 128 (weights per row of the 1-bit
+ * layout).  Returns 0 for K <= 0. */
+int64_t bl_padded_k_1bit(int64_t K);
+
+/* Bytes of a 1-bit packed binary matrix: N * Kb / 8.  0 for invalid sizes. */
+size_t bl_packed_bytes_1bit(int64_t N, int64_t K);
+
 /* Workspace bytes bitlinear_pack needs (256 64-bit exponent bins). */
 size_t bl_pack_workspace_bytes(int64_t N, int64_t K);
 
@@ -92,11 +100,17 @@ const char *bl_status_str(int status);
  *  mode     BL_TERNARY: absmean ternarisation ([P1] "Absmean量子化関数").
  *           BL_BINARY : sign binarisation, +1 for w >= 0 including -0.0
  *                       ([P1] "1-Bit重みとSign関数"); same scale g_w.
+ *           BL_BINARY_1BIT: the same binarisation in the 1-bit layout
+ *                       below (for bitlinear_forward_1bit).
  *  Wp       [N][Kp/16] uint32 words, device, 16-byte aligned, written.
  *           Layout: word j of row n covers weights 16j..16j+15; weight
  *           16j + 4s + b is stored in byte b at bits 2s..2s+1 with code
  *           t + 1 (00 = -1, 01 = 0, 10 = +1; 11 never written).  Padding
  *           weights k >= K hold code 01.
+ *           BL_BINARY_1BIT: [N][Kb/32] words (bl_packed_bytes_1bit bytes);
+ *           word j of row n covers weights 32j..32j+31; weight 32j + 4s + b
+ *           is bit 8b + s (s = 0..7, b = 0..3), 1 for +1 and 0 for -1;
+ *           padding weights k >= K are bit 0.
  *  w_scale  1 float, device, written with g_w (the scale itself, not its
  *           reciprocal).
  *  ws       device workspace, 16-byte aligned, >= bl_pack_workspace_bytes;
@@ -145,6 +159,22 @@ int bitlinear_quant_act(const void *X, int dtype, int64_t M, int64_t K, int8_t *
 int bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                       int64_t M, int64_t K, const uint32_t *Wp, const float *w_scale,
                       int64_t N, float *Y, int32_t *acc_out, void *stream);
+
+/*
+ * bitlinear_forward_1bit -- bitlinear_forward for binary weights packed by
+ * bitlinear_pack(..., BL_BINARY_1BIT, ...) ([P1] "1-Bit重みとSign関数":
+ * t = +1 / -1 in one bit; the integer product is again sum_pos - sum_neg,
+ * [P3] §3.1).  Same arguments, except
+ *  Wb       [N][Kb/32] words of the 1-bit layout (Kb = bl_padded_k_1bit(K)),
+ *           16-byte aligned.
+ *  The kernel is chosen by M (1: the bit GEMV; otherwise the 1-bit MFMA
+ *  kernel in slices of up to 64 tokens); the results equal those of the
+ *  2-bit layout of the same weights bit for bit.
+ *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EHIP.
+ */
+int bitlinear_forward_1bit(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                           int64_t M, int64_t K, const uint32_t *Wb, const float *w_scale,
+                           int64_t N, float *Y, int32_t *acc_out, void *stream);
 
 /* bitlinear_forward with the kernel chosen by the caller (for cross-checks
  * and timing): BL_KERNEL_AUTO as bitlinear_forward; BL_KERNEL_GEMV needs

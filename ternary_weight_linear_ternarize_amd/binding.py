@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbitlinear.so")
 
 BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP = range(6)
-BL_TERNARY, BL_BINARY = 0, 1
+BL_TERNARY, BL_BINARY, BL_BINARY_1BIT = 0, 1, 2
 BL_F32, BL_BF16 = 0, 1
 BL_KERNEL_AUTO, BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_TILED = range(4)
 FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "HN", "GH", "QH", "RSH", "GHP", "PART")
@@ -43,6 +43,10 @@ def lib():
     L.bl_padded_k.restype = I64
     L.bl_packed_bytes.argtypes = [I64, I64]
     L.bl_packed_bytes.restype = SZ
+    L.bl_padded_k_1bit.argtypes = [I64]
+    L.bl_padded_k_1bit.restype = I64
+    L.bl_packed_bytes_1bit.argtypes = [I64, I64]
+    L.bl_packed_bytes_1bit.restype = SZ
     L.bl_pack_workspace_bytes.argtypes = [I64, I64]
     L.bl_pack_workspace_bytes.restype = SZ
     L.bl_status_str.argtypes = [I]
@@ -53,6 +57,8 @@ def lib():
     L.bitlinear_quant_act.restype = I
     L.bitlinear_forward.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, P]
     L.bitlinear_forward.restype = I
+    L.bitlinear_forward_1bit.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, P]
+    L.bitlinear_forward_1bit.restype = I
     L.bitlinear_forward_kernel.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, I, P]
     L.bitlinear_forward_kernel.restype = I
     L.bitlinear_fused_workspace_bytes.argtypes = [I64, I64]
@@ -111,11 +117,12 @@ def ffn_workspace_layout(M, D, F):
 # entry points (same names as the C ABI)
 
 def bitlinear_pack(W, mode=BL_TERNARY, out=None, scale=None, ws=None):
-    """Quantise and pack W [N, K] float32 -> (Wp uint32 [N, Kp/16] as int32, w_scale [1])."""
+    """Quantise and pack W [N, K] float32 -> (Wp uint32 [N, Kp/16] as int32, w_scale [1]);
+    with mode BL_BINARY_1BIT the words are [N, Kb/32] (1-bit layout)."""
     N, K = W.shape
-    kp = padded_k(K)
     dev = W.device
-    Wp = out if out is not None else torch.empty((N, kp // 16), dtype=torch.int32, device=dev)
+    words = lib().bl_padded_k_1bit(K) // 32 if mode == BL_BINARY_1BIT else padded_k(K) // 16
+    Wp = out if out is not None else torch.empty((N, words), dtype=torch.int32, device=dev)
     sc = scale if scale is not None else torch.empty(1, dtype=torch.float32, device=dev)
     nws = lib().bl_pack_workspace_bytes(N, K)
     ws = ws if ws is not None else torch.empty(nws, dtype=torch.uint8, device=dev)
@@ -160,6 +167,23 @@ def bitlinear_forward(Xq, x_scale, x_rowsum, K, Wp, w_scale, N, with_acc=False,
         _dev(Wp, "Wp"), _dev(w_scale, "w_scale"), N, _dev(Y, "Y"), _opt(acc, "acc_out"),
         int(kernel), _stream(dev))
     _check(st, "bitlinear_forward")
+    return (Y, acc) if with_acc else Y
+
+
+def bitlinear_forward_1bit(Xq, x_scale, x_rowsum, K, Wb, w_scale, N, with_acc=False, out=None,
+                           acc_out=None):
+    """As bitlinear_forward for binary weights in the 1-bit layout."""
+    M = Xq.shape[0]
+    dev = Xq.device
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    acc = acc_out
+    if with_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    st = lib().bitlinear_forward_1bit(
+        _dev(Xq, "Xq"), _dev(x_scale, "x_scale"), _dev(x_rowsum, "x_rowsum"), M, K,
+        _dev(Wb, "Wb"), _dev(w_scale, "w_scale"), N, _dev(Y, "Y"), _opt(acc, "acc_out"),
+        _stream(dev))
+    _check(st, "bitlinear_forward_1bit")
     return (Y, acc) if with_acc else Y
 
 

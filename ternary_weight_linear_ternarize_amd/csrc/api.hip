@@ -39,6 +39,13 @@ size_t bl_packed_bytes(int64_t N, int64_t K) {
   return (size_t)N * (size_t)padk(K) / 4;
 }
 
+int64_t bl_padded_k_1bit(int64_t K) { return K <= 0 ? 0 : (K + 127) / 128 * 128; }
+
+size_t bl_packed_bytes_1bit(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)N * (size_t)bl_padded_k_1bit(K) / 8;
+}
+
 size_t bl_pack_workspace_bytes(int64_t N, int64_t K) {
   (void)N;
   (void)K;
@@ -60,13 +67,14 @@ const char* bl_status_str(int status) {
 int bitlinear_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp, float* w_scale,
                    void* ws, size_t ws_bytes, void* stream) {
   if (!W || !Wp || !w_scale) return BL_EINVAL;
-  if (mode != BL_TERNARY && mode != BL_BINARY) return BL_EINVAL;
+  if (mode != BL_TERNARY && mode != BL_BINARY && mode != BL_BINARY_1BIT) return BL_EINVAL;
   if (!dim_ok(N) || !dim_ok(K)) return BL_ESHAPE;
   if (!ws || ws_bytes < bl_pack_workspace_bytes(N, K)) return BL_EWORKSPACE;
   if (!aligned(W, 4) || !aligned(Wp, 16) || !aligned(w_scale, 4) || !aligned(ws, 16))
     return BL_EALIGN;
-  return hip_status(bl::launch_pack(W, N, K, mode == BL_BINARY, Wp, w_scale,
-                                    reinterpret_cast<uint64_t*>(ws), as_stream(stream)));
+  const int kind = mode == BL_TERNARY ? 0 : (mode == BL_BINARY ? 1 : 2);
+  return hip_status(bl::launch_pack(W, N, K, kind, Wp, w_scale, reinterpret_cast<uint64_t*>(ws),
+                                    as_stream(stream)));
 }
 
 int bitlinear_quant_act(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
@@ -110,6 +118,16 @@ int bitlinear_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_r
                       int32_t* acc_out, void* stream) {
   return bitlinear_forward_kernel(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y, acc_out,
                                   BL_KERNEL_AUTO, stream);
+}
+
+int bitlinear_forward_1bit(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
+                           int64_t M, int64_t K, const uint32_t* Wb, const float* w_scale,
+                           int64_t N, float* Y, int32_t* acc_out, void* stream) {
+  int st = check_forward(Xq, x_scale, x_rowsum, M, K, Wb, w_scale, N, Y);
+  if (st != BL_OK) return st;
+  if (acc_out && !aligned(acc_out, 4)) return BL_EALIGN;
+  return hip_status(bl::launch_forward_1bit(Xq, x_scale, x_rowsum, M, K, Wb, w_scale, N, Y,
+                                            acc_out, as_stream(stream)));
 }
 
 size_t bitlinear_fused_workspace_offset(int64_t M, int64_t K, int which) {

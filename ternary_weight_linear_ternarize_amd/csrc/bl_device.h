@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bl {
 
 // Scale offset added before dividing (youngju.dev "Absmean量子化関数" and
@@ -34,6 +36,14 @@ typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 __device__ __forceinline__ buf_rsrc make_buf_rsrc(const void* base, uint32_t nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
                                            0x00020000);
+}
+
+// s_waitcnt operand that waits until at most n (< 64) vector memory
+// operations of this wave are outstanding and leaves the other counters
+// alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8).
+__host__ __device__ constexpr int vmcnt_only(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
 // LDS bytes stage_rows_lds writes for M rows of the given pitch.
@@ -580,5 +590,73 @@ struct Dot16 {
   }
   __device__ __forceinline__ int total() const { return a0 + (a1 >> 2) + (a2 >> 4) + a3; }
 };
+
+// Sum of q over the set bits of 1-bit packed words (binary weights): word w
+// holds 32 weights, weight 4s + b at bit 8b + s, against the activation codes
+// x[0..7] (dword s = the codes of weights 4s .. 4s+3).  Bit s of every byte
+// is masked in place, so group s enters its dot product scaled by 2^(s % 4)
+// (groups 4..7 after one shift by 4); the four scaled sums are rescaled
+// exactly at the end.  Bytes stay <= 8, so the signed dot product is exact.
+struct DotBits32 {
+  int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  __device__ __forceinline__ void add(uint32_t w, const int4& lo, const int4& hi) {
+    a0 = __builtin_amdgcn_sdot4((int)(w & 0x01010101u), lo.x, a0, false);
+    a1 = __builtin_amdgcn_sdot4((int)(w & 0x02020202u), lo.y, a1, false);
+    a2 = __builtin_amdgcn_sdot4((int)(w & 0x04040404u), lo.z, a2, false);
+    a3 = __builtin_amdgcn_sdot4((int)(w & 0x08080808u), lo.w, a3, false);
+    const uint32_t w4 = w >> 4;
+    a0 = __builtin_amdgcn_sdot4((int)(w4 & 0x01010101u), hi.x, a0, false);
+    a1 = __builtin_amdgcn_sdot4((int)(w4 & 0x02020202u), hi.y, a1, false);
+    a2 = __builtin_amdgcn_sdot4((int)(w4 & 0x04040404u), hi.z, a2, false);
+    a3 = __builtin_amdgcn_sdot4((int)(w4 & 0x08080808u), hi.w, a3, false);
+  }
+  __device__ __forceinline__ int total() const { return a0 + (a1 >> 1) + (a2 >> 2) + (a3 >> 3); }
+};
+
+// Reduce v[0..R) (per-lane partials of R rows) across the 64 lanes with a
+// transposing butterfly on DPP / lane-swap moves, small strides first: the
+// first log2 R steps exchange halves of the row set, the rest add.  On return
+// every lane l holds the full sum of row gemv_row<R>(l) in v[0] (the low
+// log2 R bits of l, bit-reversed).
+template <int R>
+__device__ __forceinline__ int wave_transpose_reduce(int (&v)[R]) {
+  const int lane = threadIdx.x & 63;
+  int cnt = R;
+  auto step = [&](auto o_tag) {
+    constexpr int O = decltype(o_tag)::value;
+    if (cnt > 1) {
+      const int half = cnt >> 1;
+      const bool hi = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i) {
+        if (i < half) {
+          const int keep = hi ? v[half + i] : v[i];
+          const int send = hi ? v[i] : v[half + i];
+          v[i] = keep + dpp::xchg<O>(send);
+        }
+      }
+      cnt = half;
+    } else {
+      v[0] += dpp::xchg<O>(v[0]);
+    }
+  };
+  step(std::integral_constant<int, 1>());
+  step(std::integral_constant<int, 2>());
+  step(std::integral_constant<int, 4>());
+  step(std::integral_constant<int, 8>());
+  step(std::integral_constant<int, 16>());
+  step(std::integral_constant<int, 32>());
+  return v[0];
+}
+
+// Row whose total lane l holds after wave_transpose_reduce<R>.
+template <int R>
+__device__ __forceinline__ int gemv_row(int lane) {
+  constexpr int LOGR = (R == 1) ? 0 : (R == 2) ? 1 : (R == 4) ? 2 : (R == 8) ? 3 : 4;
+  int r = 0;
+#pragma unroll
+  for (int b = 0; b < LOGR; ++b) r |= ((lane >> b) & 1) << (LOGR - 1 - b);
+  return r;
+}
 
 }  // namespace bl

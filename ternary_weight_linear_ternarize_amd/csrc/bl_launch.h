@@ -8,9 +8,17 @@
 namespace bl {
 
 // bitlinear_pack: zero bins, exponent-binned exact |w| sum, finalize g_w,
-// ternarise/binarise + pack.
-hipError_t launch_pack(const float* W, int64_t N, int64_t K, int binary, uint32_t* Wp,
+// ternarise/binarise + pack.  mode 0: ternary, 1: binary (2-bit codes),
+// 2: binary in the 1-bit layout.
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp,
                        float* w_scale, uint64_t* bins, hipStream_t s);
+
+// Y = dequant(Xq . T^T) for binary weights in the 1-bit layout (rows of
+// Kb = K rounded up to 128 weights; Xq rows of Kp = K rounded up to 64):
+// the bit GEMV for one token, the 1-bit MFMA kernel otherwise (bin1.hip).
+hipError_t launch_forward_1bit(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
+                               int64_t M, int64_t K, const uint32_t* Wb, const float* w_scale,
+                               int64_t N, float* Y, int32_t* acc_out, hipStream_t s);
 
 // Per-token absmax int8 quantisation.  When gamma_parts is non-null the
 // scale of row m is max over p < nparts of gamma_parts[p * M + m] (partial

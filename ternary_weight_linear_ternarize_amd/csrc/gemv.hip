@@ -26,8 +26,6 @@
 //            (identical bits) into LDS -- one launch per layer;
 //   XS_PARTS float activations whose scale is the maximum of per-block partial
 //            maxima written by the previous kernel (the FFN's h).
-#include <type_traits>
-
 #include "bl_device.h"
 #include "bl_launch.h"
 
@@ -37,52 +35,6 @@ enum { EPI_STORE = 0, EPI_GATEUP = 1 };
 enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3 };
 
 constexpr int kFusedMaxKp = 7168;  // largest padded K quantised inside the GEMV
-
-// Reduce v[0..R) (per-lane partials of R rows) across the 64 lanes with a
-// transposing butterfly on DPP / lane-swap moves, small strides first: the
-// first log2 R steps exchange halves of the row set, the rest add.  On return
-// every lane l holds the full sum of row gemv_row<R>(l) in v[0] (the low
-// log2 R bits of l, bit-reversed).
-template <int R>
-__device__ __forceinline__ int wave_transpose_reduce(int (&v)[R]) {
-  const int lane = threadIdx.x & 63;
-  int cnt = R;
-  auto step = [&](auto o_tag) {
-    constexpr int O = decltype(o_tag)::value;
-    if (cnt > 1) {
-      const int half = cnt >> 1;
-      const bool hi = (lane & O) != 0;
-#pragma unroll
-      for (int i = 0; i < R / 2; ++i) {
-        if (i < half) {
-          const int keep = hi ? v[half + i] : v[i];
-          const int send = hi ? v[i] : v[half + i];
-          v[i] = keep + dpp::xchg<O>(send);
-        }
-      }
-      cnt = half;
-    } else {
-      v[0] += dpp::xchg<O>(v[0]);
-    }
-  };
-  step(std::integral_constant<int, 1>());
-  step(std::integral_constant<int, 2>());
-  step(std::integral_constant<int, 4>());
-  step(std::integral_constant<int, 8>());
-  step(std::integral_constant<int, 16>());
-  step(std::integral_constant<int, 32>());
-  return v[0];
-}
-
-// Row whose total lane l holds after wave_transpose_reduce<R>.
-template <int R>
-__device__ __forceinline__ int gemv_row(int lane) {
-  constexpr int LOGR = (R == 1) ? 0 : (R == 2) ? 1 : (R == 4) ? 2 : (R == 8) ? 3 : 4;
-  int r = 0;
-#pragma unroll
-  for (int b = 0; b < LOGR; ++b) r |= ((lane >> b) & 1) << (LOGR - 1 - b);
-  return r;
-}
 
 __device__ __forceinline__ float block_max4(float v, float* red) {
   v = dpp::max_nonneg_f32(v);

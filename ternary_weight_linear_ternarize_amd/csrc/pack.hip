@@ -1,4 +1,5 @@
-// Weight quantisation and 2-bit packing on gfx950.
+// Weight quantisation and packing (2-bit codes; 1-bit for binary weights) on
+// gfx950.
 //
 // youngju.dev "BitNet論文分析", section "Absmean量子化関数": the ternary
 // weight scale is the mean of |W| over the whole tensor; codes are
@@ -89,7 +90,27 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   Wp[idx] = word;
 }
 
-hipError_t launch_pack(const float* W, int64_t N, int64_t K, int binary, uint32_t* Wp,
+// 1-bit layout of binary weights, one thread per word: row n, word j covers
+// weights 32j..32j+31; weight 32j + 4s + b is bit 8b + s, 1 for w >= 0 (+1)
+// and 0 for w < 0 (-1); weights past K (rows padded to 128) are bit 0.
+__global__ __launch_bounds__(256) void pack1_kernel(const float* __restrict__ W, int64_t N,
+                                                    int64_t K, int64_t words_per_row,
+                                                    uint32_t* __restrict__ Wp) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * words_per_row) return;
+  const int64_t n = idx / words_per_row, j = idx - n * words_per_row;
+  const float* row = W + n * K;
+  uint32_t word = 0u;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int64_t k = 32 * j + r;
+    const uint32_t bit = (k < K && row[k] >= 0.0f) ? 1u : 0u;
+    word |= bit << (8 * (r & 3) + (r >> 2));
+  }
+  Wp[idx] = word;
+}
+
+hipError_t launch_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp,
                        float* w_scale, uint64_t* bins, hipStream_t s) {
   const int64_t n = N * K;
   const int64_t kp = (K + 63) / 64 * 64;
@@ -99,9 +120,15 @@ hipError_t launch_pack(const float* W, int64_t N, int64_t K, int binary, uint32_
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(absmean_bins_kernel, dim3((unsigned)blocks), dim3(256), 0, s, W, n, bins);
   hipLaunchKernelGGL(absmean_finalize_kernel, dim3(1), dim3(64), 0, s, bins, n, w_scale);
+  if (mode == 2) {
+    const int64_t wpr1 = (K + 127) / 128 * 4;
+    const unsigned b1 = (unsigned)((N * wpr1 + 255) / 256);
+    hipLaunchKernelGGL(pack1_kernel, dim3(b1), dim3(256), 0, s, W, N, K, wpr1, Wp);
+    return hipGetLastError();
+  }
   const int64_t total = N * wpr;
   const unsigned pblocks = (unsigned)((total + 255) / 256);
-  if (binary)
+  if (mode == 1)
     hipLaunchKernelGGL(pack_kernel<true>, dim3(pblocks), dim3(256), 0, s, W, N, K, wpr, w_scale, Wp);
   else
     hipLaunchKernelGGL(pack_kernel<false>, dim3(pblocks), dim3(256), 0, s, W, N, K, wpr, w_scale, Wp);

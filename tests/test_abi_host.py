@@ -42,6 +42,10 @@ def test_size_helpers():
     assert lib.bl_packed_bytes(28672, 8192) == 58720256
     assert lib.bl_packed_bytes(400, 512) == 51200
     assert lib.bl_pack_workspace_bytes(10, 10) >= 256 * 8
+    assert lib.bl_padded_k_1bit(1) == 128 and lib.bl_padded_k_1bit(128) == 128
+    assert lib.bl_padded_k_1bit(129) == 256 and lib.bl_padded_k_1bit(0) == 0
+    assert lib.bl_packed_bytes_1bit(28672, 8192) == 29360128
+    assert lib.bl_packed_bytes_1bit(400, 500) == 400 * 512 // 8
     total, off = B.ffn_workspace_layout(8, 2560, 6912)
     assert all(v % 256 == 0 for v in off.values())
     assert off["QX"] - off["XN"] >= 8 * 2560 * 4
@@ -96,6 +100,11 @@ def test_forward_validation():
     assert f(*a, B.BL_KERNEL_SKINNY, None) == B.BL_ESHAPE  # skinny needs M <= 64
     assert f(*args, 9, None) == B.BL_EINVAL
     assert lib.bitlinear_forward(FAKE, FAKE, FAKE, 1, 64, ODD, FAKE, 16, FAKE, None, None) == B.BL_EALIGN
+    g = lib.bitlinear_forward_1bit
+    assert g(FAKE, FAKE, None, 1, 64, FAKE, FAKE, 16, FAKE, None, None) == B.BL_EINVAL
+    assert g(FAKE, FAKE, FAKE, 0, 64, FAKE, FAKE, 16, FAKE, None, None) == B.BL_ESHAPE
+    assert g(FAKE, FAKE, FAKE, 1, 64, ODD, FAKE, 16, FAKE, None, None) == B.BL_EALIGN
+    assert g(FAKE, FAKE, FAKE, 1, 64, FAKE, FAKE, 16, FAKE, ODD, None) == B.BL_EALIGN
 
 
 def test_ffn_validation():

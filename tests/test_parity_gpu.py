@@ -306,3 +306,69 @@ def test_forward_fused_from_float(M, K, N, bf16):
     assert_rel(host(Y), y)
     Y2, _ = B.bitlinear_forward_fused(xd, Wp, sc, N)
     np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
+# ----------------------------------------------------------------------------
+# binary weights in the 1-bit layout
+
+def check_pack1(W):
+    g = oracle.weight_scale(W)
+    t = oracle.binarize(W)
+    p = oracle.pack1(t)
+    Wb, sc = gpu_pack(W, B.BL_BINARY_1BIT)
+    np.testing.assert_array_equal(host(Wb).view(np.uint32), p)
+    assert host(sc)[0].view(np.uint32) == np.float32(g).view(np.uint32)
+    return g, t, Wb, sc
+
+
+def check_forward1(q, gx, t, gw, Xq, xs, xr, Wb, ws):
+    K = q.shape[1]
+    N = t.shape[0]
+    acc = oracle.int_linear(q, t)
+    y = oracle.dequant(acc, gx, gw)
+    Y, A = B.bitlinear_forward_1bit(Xq, xs, xr, K, Wb, ws, N, with_acc=True)
+    np.testing.assert_array_equal(host(A), acc)
+    assert_rel(host(Y), y)
+    Y2 = B.bitlinear_forward_1bit(Xq, xs, xr, K, Wb, ws, N)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+    return Y
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 1, 1), (1, 64, 5), (1, 127, 33), (1, 129, 300), (1, 2560, 700), (1, 8192, 100),
+    (1, 8320, 70), (1, 24640, 20), (1, 40000, 9), (2, 64, 16), (5, 129, 64), (8, 1040, 257),
+    (16, 512, 400), (17, 63, 15), (33, 1000, 100), (64, 2560, 96), (65, 300, 130),
+    (100, 1040, 257), (130, 128, 70),
+])
+def test_binary_1bit_ragged_shapes(M, K, N):
+    d = synth.random_case(4000 + M * 7 + N, M, K, N)
+    g, t, Wb, sc = check_pack1(d["W"])
+    q, gx, rs, Xq, xs, xr = check_quant(d["X"])
+    Y = check_forward1(q, gx, t, g, Xq, xs, xr, Wb, sc)
+    # the 2-bit layout of the same binary weights gives the same bits
+    g2, t2, Wp, sc2 = check_pack(d["W"], "binary")
+    Y2 = B.bitlinear_forward(Xq, xs, xr, K, Wp, sc2, N)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
+def test_binary_1bit_signed_zero_and_degenerate_rows():
+    W = synth.normal(31, 2, (40, 300))
+    W[2, :] = 0.0
+    W[3, :] = -0.0
+    W[4, :] = -1.0
+    g, t, Wb, sc = check_pack1(W)
+    assert (t[2] == 1).all() and (t[3] == 1).all() and (t[4] == -1).all()
+    X = synth.normal(31, 1, (3, 300))
+    X[1] = 0.0
+    q, gx, rs, Xq, xs, xr = check_quant(X)
+    check_forward1(q, gx, t, g, Xq, xs, xr, Wb, sc)
+
+
+def test_decode_100b_binary_1bit_full():
+    d = synth.decode_100b()
+    g, t, Wb, sc = check_pack1(d["W"])
+    del d["W"]
+    assert host(Wb).nbytes == 28672 * 8192 // 8
+    for M in (1, 8):
+        q, gx, rs, Xq, xs, xr = check_quant(d["X"][:M])
+        check_forward1(q, gx, t, g, Xq, xs, xr, Wb, sc)
