@@ -58,6 +58,8 @@ def _load():
     lib.orc_unpack1.argtypes = [P, I64, I64, P]
     lib.orc_unpack1.restype = I64
     lib.orc_act_quant.argtypes = [P, I64, I64, P, P, P]
+    lib.orc_act_quant_a48.argtypes = [P, I64, I64, I64, P, P, P, P, P, P, P]
+    lib.orc_dequant_a48.argtypes = [P, P, P, P, F, I64, I64, P]
     lib.orc_int_linear.argtypes = [P, P, I64, I64, I64, P]
     lib.orc_dequant.argtypes = [P, P, F, I64, I64, P]
     lib.orc_rmsnorm.argtypes = [P, P, F, I64, I64, P]
@@ -179,6 +181,43 @@ def act_quant(x):
     rs = np.empty(M, dtype=np.int32)
     _load().orc_act_quant(_ptr(x), M, K, _ptr(q), _ptr(g), _ptr(rs))
     return q, g, rs
+
+
+def act_quant_a48(x, n_out):
+    """BitNet a4.8 split quantisation of x [M, K]: the n_out largest |x| per
+    row (ties to the lower index) in int8, the rest in int4 ([-7, 7]).
+
+    Returns dict q4, g4, rs4, q8, g8, rs8, outlier (uint8 mask)."""
+    x = _f32(x)
+    M, K = x.shape
+    r = {"q4": np.empty((M, K), np.int8), "g4": np.empty(M, np.float32),
+         "rs4": np.empty(M, np.int32), "q8": np.empty((M, K), np.int8),
+         "g8": np.empty(M, np.float32), "rs8": np.empty(M, np.int32),
+         "outlier": np.empty((M, K), np.uint8)}
+    _load().orc_act_quant_a48(_ptr(x), M, K, int(n_out), _ptr(r["q4"]), _ptr(r["g4"]),
+                              _ptr(r["rs4"]), _ptr(r["q8"]), _ptr(r["g8"]), _ptr(r["rs8"]),
+                              _ptr(r["outlier"]))
+    return r
+
+
+def dequant_a48(acc4, g4, acc8, g8, gamma_w):
+    acc4 = np.ascontiguousarray(acc4, dtype=np.int32)
+    acc8 = np.ascontiguousarray(acc8, dtype=np.int32)
+    M, N = acc4.shape
+    y = np.empty((M, N), dtype=np.float32)
+    _load().orc_dequant_a48(_ptr(acc4), _ptr(_f32(g4).reshape(-1)), _ptr(acc8),
+                            _ptr(_f32(g8).reshape(-1)), float(np.float32(gamma_w)), M, N, _ptr(y))
+    return y
+
+
+def bitlinear_a48(x, t, gamma_w, n_out):
+    """BitLinear with a4.8 activations: returns the quantiser's outputs, both
+    accumulators and y."""
+    r = act_quant_a48(x, n_out)
+    r["acc4"] = int_linear(r["q4"], t)
+    r["acc8"] = int_linear(r["q8"], t)
+    r["y"] = dequant_a48(r["acc4"], r["g4"], r["acc8"], r["g8"], gamma_w)
+    return r
 
 
 def int_linear(q, t):

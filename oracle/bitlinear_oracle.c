@@ -274,6 +274,86 @@ void orc_act_quant(const float *x, int64_t M, int64_t K, int8_t *q, float *gamma
     }
 }
 
+/* [P1] "BitNet a4.8": activations in 4 bits, with the top fraction of the
+ * values (the outliers) split off and kept in 8 bits.  Reading of this build
+ * (the page gives no formulas): per token row, the n_out entries of largest
+ * |x| (ties to the lower index) are outliers; they are quantised like
+ * activation_quant with Q = 127 and their own scale g8 = their max |x|; all
+ * other entries are quantised with Q = 7 (symmetric 4-bit range [-7, 7]) and
+ * the scale g4 = max |x| over them.  Each code vector is zero where the
+ * other one holds the entry.  outlier [M][K] receives 1 at the outliers. */
+static const float *orc_sort_row;
+
+static int orc_outlier_order(const void *a, const void *b) {
+    int64_t i = *(const int64_t *)a, j = *(const int64_t *)b;
+    float u = fabsf(orc_sort_row[i]), v = fabsf(orc_sort_row[j]);
+    if (u > v) return -1;
+    if (u < v) return 1;
+    return (i < j) ? -1 : (i > j);
+}
+
+void orc_act_quant_a48(const float *x, int64_t M, int64_t K, int64_t n_out, int8_t *q4,
+                       float *g4, int32_t *rs4, int8_t *q8, float *g8, int32_t *rs8,
+                       uint8_t *outlier) {
+    int64_t *order = (int64_t *)malloc(sizeof(int64_t) * (size_t)(K > 0 ? K : 1));
+    if (n_out > K) n_out = K;
+    if (n_out < 0) n_out = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        const float *xr = x + m * K;
+        uint8_t *out = outlier + m * K;
+        for (int64_t k = 0; k < K; ++k) order[k] = k;
+        orc_sort_row = xr;
+        qsort(order, (size_t)K, sizeof(int64_t), orc_outlier_order);
+        for (int64_t k = 0; k < K; ++k) out[k] = 0;
+        for (int64_t j = 0; j < n_out; ++j) out[order[j]] = 1;
+        float a8 = 0.0f, a4 = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(xr[k]);
+            if (out[k]) { if (a > a8) a8 = a; }
+            else if (a > a4) a4 = a;
+        }
+        float d8 = a8 + ORC_EPS, d4 = a4 + ORC_EPS;
+        int32_t s4 = 0, s8 = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            int8_t c4 = 0, c8 = 0;
+            if (out[k]) {
+                float r = nearbyintf((xr[k] * ORC_Q) / d8);
+                if (r > ORC_Q) r = ORC_Q;
+                if (r < -ORC_Q) r = -ORC_Q;
+                c8 = (int8_t)r;
+            } else {
+                float r = nearbyintf((xr[k] * 7.0f) / d4);
+                if (r > 7.0f) r = 7.0f;
+                if (r < -7.0f) r = -7.0f;
+                c4 = (int8_t)r;
+            }
+            q4[m * K + k] = c4;
+            q8[m * K + k] = c8;
+            s4 += c4;
+            s8 += c8;
+        }
+        g4[m] = a4;
+        g8[m] = a8;
+        if (rs4) rs4[m] = s4;
+        if (rs8) rs8[m] = s8;
+    }
+    free(order);
+}
+
+/* The a4.8 output: each part dequantised as [P1]'s listing does
+ * (output * (w_scale * x_scale) / Q, left to right), then the two added. */
+void orc_dequant_a48(const int32_t *acc4, const float *g4, const int32_t *acc8, const float *g8,
+                     float gamma_w, int64_t M, int64_t N, float *y) {
+    for (int64_t m = 0; m < M; ++m) {
+        float s4 = gamma_w * g4[m], s8 = gamma_w * g8[m];
+        for (int64_t n = 0; n < N; ++n) {
+            float y4 = ((float)acc4[m * N + n] * s4) / 7.0f;
+            float y8 = ((float)acc8[m * N + n] * s8) / ORC_Q;
+            y[m * N + n] = y4 + y8;
+        }
+    }
+}
+
 /* [P1] F.linear(x_q, w_q) with no bias ([P5]): acc[m][n] = sum_k q[m][k] *
  * t[n][k], an exact integer sum.  W is [N][K] (out, in) as in the listings'
  * nn.Parameter(out_features, in_features). */

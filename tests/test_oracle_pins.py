@@ -563,6 +563,75 @@ def test_subln_off_leaves_the_block_unchanged():
 
 
 # ----------------------------------------------------------------------------
+# BitNet a4.8 activations: top-n_out |x| per row in int8, the rest in int4
+
+def test_a48_hand_worked_row():
+    x = np.array([[7.0, 3.5, -7.0, 1.0, 0.0, 100.0, -2.5, 0.5]], np.float32)
+    r = oracle.act_quant_a48(x, 1)
+    np.testing.assert_array_equal(r["outlier"][0], [0, 0, 0, 0, 0, 1, 0, 0])
+    assert r["g8"][0] == 100.0 and r["g4"][0] == 7.0
+    # 127*100/100.00001 -> 127; 7*7/7.00001 = 6.99999 -> 7; 24.5/7.00001 = 3.4999950 -> 3;
+    # -17.5/7.00001 = -2.4999964 -> -2; 3.5/7.00001 = 0.4999993 -> 0
+    np.testing.assert_array_equal(r["q8"][0], [0, 0, 0, 0, 0, 127, 0, 0])
+    np.testing.assert_array_equal(r["q4"][0], [7, 3, -7, 1, 0, 0, -2, 0])
+    assert r["rs4"][0] == 2 and r["rs8"][0] == 127
+    # two outliers: |7| at index 0 and |-7| at index 2 tie, the lower index wins;
+    # 7*127/100.00001 = 8.8899991 -> 9
+    r = oracle.act_quant_a48(x, 2)
+    np.testing.assert_array_equal(r["outlier"][0], [1, 0, 0, 0, 0, 1, 0, 0])
+    np.testing.assert_array_equal(r["q8"][0], [9, 0, 0, 0, 0, 127, 0, 0])
+    np.testing.assert_array_equal(r["q4"][0], [0, 3, -7, 1, 0, 0, -2, 0])
+
+
+def test_a48_split_is_the_top_n_by_magnitude():
+    rng = np.random.default_rng(12)
+    for K, n_out in ((1, 0), (1, 1), (40, 3), (300, 0), (300, 3), (2560, 26), (2560, 2560), (1000, 999)):
+        x = synth.normal(40 + K, 1, (4, K))
+        x[1] = np.round(x[1] * 2) / 2  # many ties in |x|
+        x[2, ::7] *= np.float32(20.0)  # outlier channels
+        r = oracle.act_quant_a48(x, n_out)
+        for m in range(4):
+            a = np.abs(x[m])
+            order = np.lexsort((np.arange(K), -a))  # |x| descending, then index
+            want = np.zeros(K, np.uint8)
+            want[order[:n_out]] = 1
+            np.testing.assert_array_equal(r["outlier"][m], want)
+            out = want.astype(bool)
+            assert r["g8"][m] == (a[out].max() if out.any() else 0.0)
+            assert r["g4"][m] == (a[~out].max() if (~out).any() else 0.0)
+            assert not r["q4"][m][out].any() and not r["q8"][m][~out].any()
+            assert np.abs(r["q4"][m]).max(initial=0) <= 7 and np.abs(r["q8"][m]).max(initial=0) <= 127
+            assert r["rs4"][m] == int(r["q4"][m].astype(np.int64).sum())
+            assert r["rs8"][m] == int(r["q8"][m].astype(np.int64).sum())
+            # the largest inlier reaches the end of the 4-bit range
+            if (~out).any() and r["g4"][m] > 1e-3:
+                assert np.abs(r["q4"][m]).max() == 7
+
+
+def test_a48_all_outliers_is_the_int8_quantiser():
+    x = synth.normal(41, 1, (5, 700))
+    r = oracle.act_quant_a48(x, 700)
+    q, g, rs = oracle.act_quant(x)
+    np.testing.assert_array_equal(r["q8"], q)
+    np.testing.assert_array_equal(r["g8"], g)
+    np.testing.assert_array_equal(r["rs8"], rs)
+    assert not r["q4"].any() and not r["g4"].any()
+    _, t, _ = oracle.quantize_weights(synth.normal(41, 2, (30, 700), 0.02))
+    b = oracle.bitlinear_a48(x, t, np.float32(0.01), 700)
+    ref = oracle.bitlinear(x, t, np.float32(0.01))
+    np.testing.assert_array_equal(b["acc8"], ref["acc"])
+    np.testing.assert_array_equal(b["y"] + np.float32(0), ref["y"] + np.float32(0))
+
+
+def test_a48_dequant_closed_form():
+    acc4 = np.array([[7, -14, 0]], np.int32)
+    acc8 = np.array([[127, 0, -254]], np.int32)
+    y = oracle.dequant_a48(acc4, np.array([1.0], np.float32), acc8, np.array([2.0], np.float32),
+                           np.float32(1.0))
+    np.testing.assert_array_equal(y, [[3.0, -2.0, -4.0]])
+
+
+# ----------------------------------------------------------------------------
 # end-to-end on the single-layer workload (512 -> 400, 16 tokens)
 
 def test_single_layer_end_to_end_against_float_reference():
