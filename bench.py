@@ -399,6 +399,30 @@ def extra_workloads(torch, B, synth, dev):
             "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del cps, Wb
     torch.cuda.empty_cache()
+    # a4.8 split activations (1 % outliers in int8, the rest in int4): quantiser and product
+    Wp, sc = B.bitlinear_pack(Wd)
+    pb = Wp.numel() * 4
+    ncp = max(2, int(np.ceil(600e6 / pb)))
+    cps = [Wp.clone() for _ in range(ncp)]
+    n_out = int(round(0.01 * K))
+    for M in (1, 8):
+        Xm = torch.from_numpy(p["X"][:M]).to(dev)
+        q = B.bitlinear_quant_act_a48(Xm, n_out)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        wsa = torch.empty(B.lib().bitlinear_a48_workspace_bytes(M, N) // 4, dtype=torch.int32,
+                          device=dev)
+        ms = graph_time_per_launch(
+            lambda i: B.bitlinear_forward_a48(q, K, cps[i % ncp], sc, N, out=Y, ws=wsa), ncp, 5,
+            torch)
+        alg = pb + 2 * M * (K + 8) + 4 + M * N * 4
+        res[f"decode_100b_a48_M{M}"] = {
+            "avg_us": round(ms * 1e3, 2), "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "n_out": n_out}
+        qms = graph_time_per_launch(lambda i: B.bitlinear_quant_act_a48(Xm, n_out, out=q), 4, 5,
+                                    torch)
+        res[f"a48_quant_{M}x{K}"] = {"avg_us": round(qms * 1e3, 2)}
+    del cps, Wp
+    torch.cuda.empty_cache()
     del Wd
     torch.cuda.empty_cache()
 

@@ -176,6 +176,44 @@ int bitlinear_forward_1bit(const int8_t *Xq, const float *x_scale, const int32_t
                            int64_t M, int64_t K, const uint32_t *Wb, const float *w_scale,
                            int64_t N, float *Y, int32_t *acc_out, void *stream);
 
+/*
+ * bitlinear_quant_act_a48 -- BitNet a4.8 split activations ([P1] "BitNet
+ * a4.8": the top fraction of the values is split off at 8 bits, the rest is
+ * quantised to 4 bits).  Per token row m:
+ *   outliers: the n_out entries of largest |x| (ties to the lower index);
+ *   g8 = max |x| over them, q8 = clamp(rne(x * 127 / (g8 + 1e-5)), +-127);
+ *   g4 = max |x| over the rest, q4 = clamp(rne(x * 7 / (g4 + 1e-5)), +-7);
+ * each code vector is 0 where the other holds the entry (and past K).
+ *  X        [M][K] float32 / bfloat16 (dtype), device.  n_out >= 0 (values
+ *           above K mean every entry).
+ *  Xq4, Xq8 [M][Kp] int8, device, 16-byte aligned, written.
+ *  x4_scale, x8_scale [M] float (g4, g8); x4_rowsum, x8_rowsum [M] int32
+ *           (row sums of q4, q8); all written.
+ *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EHIP.
+ */
+int bitlinear_quant_act_a48(const void *X, int dtype, int64_t M, int64_t K, int64_t n_out,
+                            int8_t *Xq4, float *x4_scale, int32_t *x4_rowsum, int8_t *Xq8,
+                            float *x8_scale, int32_t *x8_rowsum, void *stream);
+
+/* Workspace bytes of bitlinear_forward_a48: 8 * M * N. */
+size_t bitlinear_a48_workspace_bytes(int64_t M, int64_t N);
+
+/*
+ * bitlinear_forward_a48 -- BitLinear on a4.8 activations and packed
+ * ternary/binary weights: acc4 = q4 . t, acc8 = q8 . t (exact int32) and
+ *   Y = (acc4 * (g_w * g4)) / 7 + (acc8 * (g_w * g8)) / 127,
+ * each part dequantised in the order of [P1]'s listing, then added.
+ *  Xq4..x8_rowsum from bitlinear_quant_act_a48; Wp, w_scale, Y as for
+ *  bitlinear_forward.
+ *  ws       >= bitlinear_a48_workspace_bytes(M, N) bytes, 16-byte aligned;
+ *           after the call it holds acc4 [M][N] then acc8 [M][N] int32.
+ *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP.
+ */
+int bitlinear_forward_a48(const int8_t *Xq4, const float *x4_scale, const int32_t *x4_rowsum,
+                          const int8_t *Xq8, const float *x8_scale, const int32_t *x8_rowsum,
+                          int64_t M, int64_t K, const uint32_t *Wp, const float *w_scale,
+                          int64_t N, float *Y, void *ws, size_t ws_bytes, void *stream);
+
 /* bitlinear_forward with the kernel chosen by the caller (for cross-checks
  * and timing): BL_KERNEL_AUTO as bitlinear_forward; BL_KERNEL_GEMV needs
  * M == 1; BL_KERNEL_SKINNY needs M <= 64 (one MFMA tile row of 16/32/64

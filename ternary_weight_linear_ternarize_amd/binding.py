@@ -59,6 +59,12 @@ def lib():
     L.bitlinear_forward.restype = I
     L.bitlinear_forward_1bit.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, P]
     L.bitlinear_forward_1bit.restype = I
+    L.bitlinear_quant_act_a48.argtypes = [P, I, I64, I64, I64, P, P, P, P, P, P, P]
+    L.bitlinear_quant_act_a48.restype = I
+    L.bitlinear_a48_workspace_bytes.argtypes = [I64, I64]
+    L.bitlinear_a48_workspace_bytes.restype = SZ
+    L.bitlinear_forward_a48.argtypes = [P, P, P, P, P, P, I64, I64, P, P, I64, P, P, SZ, P]
+    L.bitlinear_forward_a48.restype = I
     L.bitlinear_forward_kernel.argtypes = [P, P, P, I64, I64, P, P, I64, P, P, I, P]
     L.bitlinear_forward_kernel.restype = I
     L.bitlinear_fused_workspace_bytes.argtypes = [I64, I64]
@@ -185,6 +191,46 @@ def bitlinear_forward_1bit(Xq, x_scale, x_rowsum, K, Wb, w_scale, N, with_acc=Fa
         _stream(dev))
     _check(st, "bitlinear_forward_1bit")
     return (Y, acc) if with_acc else Y
+
+
+def bitlinear_quant_act_a48(X, n_out, out=None):
+    """a4.8 split quantisation of X [M, K] float32/bfloat16 -> dict of device
+    tensors q4, g4, rs4, q8, g8, rs8 (codes int8 [M, Kp])."""
+    M, K = X.shape
+    dt = _act_dtype(X)
+    dev = X.device
+    kp = padded_k(K)
+    if out is None:
+        out = {"q4": torch.empty((M, kp), dtype=torch.int8, device=dev),
+               "g4": torch.empty(M, dtype=torch.float32, device=dev),
+               "rs4": torch.empty(M, dtype=torch.int32, device=dev),
+               "q8": torch.empty((M, kp), dtype=torch.int8, device=dev),
+               "g8": torch.empty(M, dtype=torch.float32, device=dev),
+               "rs8": torch.empty(M, dtype=torch.int32, device=dev)}
+    o = out
+    st = lib().bitlinear_quant_act_a48(
+        _dev(X, "X"), dt, M, K, int(n_out), _dev(o["q4"], "Xq4"), _dev(o["g4"], "x4_scale"),
+        _dev(o["rs4"], "x4_rowsum"), _dev(o["q8"], "Xq8"), _dev(o["g8"], "x8_scale"),
+        _dev(o["rs8"], "x8_rowsum"), _stream(dev))
+    _check(st, "bitlinear_quant_act_a48")
+    return out
+
+
+def bitlinear_forward_a48(q, K, Wp, w_scale, N, out=None, ws=None):
+    """Y [M, N] float32 from a4.8 activations (dict of bitlinear_quant_act_a48)
+    -> (Y, ws) where ws holds acc4 [M, N] then acc8 [M, N] int32."""
+    M = q["q4"].shape[0]
+    dev = q["q4"].device
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    nws = lib().bitlinear_a48_workspace_bytes(M, N)
+    ws = ws if ws is not None else torch.empty(nws // 4, dtype=torch.int32, device=dev)
+    st = lib().bitlinear_forward_a48(
+        _dev(q["q4"], "Xq4"), _dev(q["g4"], "x4_scale"), _dev(q["rs4"], "x4_rowsum"),
+        _dev(q["q8"], "Xq8"), _dev(q["g8"], "x8_scale"), _dev(q["rs8"], "x8_rowsum"), M, K,
+        _dev(Wp, "Wp"), _dev(w_scale, "w_scale"), N, _dev(Y, "Y"), _dev(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream(dev))
+    _check(st, "bitlinear_forward_a48")
+    return Y, ws
 
 
 def _act_dtype(X):

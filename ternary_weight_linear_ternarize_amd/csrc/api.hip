@@ -130,6 +130,41 @@ int bitlinear_forward_1bit(const int8_t* Xq, const float* x_scale, const int32_t
                                             acc_out, as_stream(stream)));
 }
 
+int bitlinear_quant_act_a48(const void* X, int dtype, int64_t M, int64_t K, int64_t n_out,
+                            int8_t* Xq4, float* x4_scale, int32_t* x4_rowsum, int8_t* Xq8,
+                            float* x8_scale, int32_t* x8_rowsum, void* stream) {
+  if (!X || !Xq4 || !x4_scale || !x4_rowsum || !Xq8 || !x8_scale || !x8_rowsum) return BL_EINVAL;
+  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(K) || n_out < 0) return BL_ESHAPE;
+  if (!aligned(X, dtype == BL_F32 ? 4 : 2) || !aligned(Xq4, 16) || !aligned(Xq8, 16) ||
+      !aligned(x4_scale, 4) || !aligned(x4_rowsum, 4) || !aligned(x8_scale, 4) ||
+      !aligned(x8_rowsum, 4))
+    return BL_EALIGN;
+  return hip_status(bl::launch_act_quant_a48(X, dtype == BL_BF16, M, K, n_out, Xq4, x4_scale,
+                                             x4_rowsum, Xq8, x8_scale, x8_rowsum,
+                                             as_stream(stream)));
+}
+
+size_t bitlinear_a48_workspace_bytes(int64_t M, int64_t N) {
+  if (!m_ok(M) || !dim_ok(N)) return 0;
+  return (size_t)M * (size_t)N * 8;
+}
+
+int bitlinear_forward_a48(const int8_t* Xq4, const float* x4_scale, const int32_t* x4_rowsum,
+                          const int8_t* Xq8, const float* x8_scale, const int32_t* x8_rowsum,
+                          int64_t M, int64_t K, const uint32_t* Wp, const float* w_scale,
+                          int64_t N, float* Y, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_forward(Xq4, x4_scale, x4_rowsum, M, K, Wp, w_scale, N, Y);
+  if (st != BL_OK) return st;
+  if (!Xq8 || !x8_scale || !x8_rowsum) return BL_EINVAL;
+  if (!aligned(Xq8, 16) || !aligned(x8_scale, 4) || !aligned(x8_rowsum, 4)) return BL_EALIGN;
+  if (!ws || ws_bytes < bitlinear_a48_workspace_bytes(M, N)) return BL_EWORKSPACE;
+  if (!aligned(ws, 16)) return BL_EALIGN;
+  return hip_status(bl::launch_forward_a48(Xq4, x4_scale, x4_rowsum, Xq8, x8_scale, x8_rowsum, M,
+                                           K, Wp, w_scale, N, Y, reinterpret_cast<int32_t*>(ws),
+                                           as_stream(stream)));
+}
+
 size_t bitlinear_fused_workspace_offset(int64_t M, int64_t K, int which) {
   if (!m_ok(M) || !dim_ok(K)) return 0;
   const size_t q = up256((size_t)M * (size_t)padk(K));

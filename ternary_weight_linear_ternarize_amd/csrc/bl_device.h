@@ -591,6 +591,33 @@ struct Dot16 {
   __device__ __forceinline__ int total() const { return a0 + (a1 >> 2) + (a2 >> 4) + a3; }
 };
 
+// Dot16 against two code vectors at once (x and z, e.g. the 4-bit and the
+// 8-bit parts of split activations): the masked weight fields are shared.
+struct Dot16x2 {
+  Dot16 x, z;
+  __device__ __forceinline__ void add(uint32_t w, const int4& xv, const int4& zv) {
+    const int m0 = (int)(w & 0x03030303u), m1 = (int)(w & 0x0c0c0c0cu);
+    const int m2 = (int)(w & 0x30303030u), m3 = (int)((w >> 6) & 0x03030303u);
+    x.a0 = __builtin_amdgcn_sdot4(m0, xv.x, x.a0, false);
+    x.a1 = __builtin_amdgcn_sdot4(m1, xv.y, x.a1, false);
+    x.a2 = __builtin_amdgcn_sdot4(m2, xv.z, x.a2, false);
+    x.a3 = __builtin_amdgcn_sdot4(m3, xv.w, x.a3, false);
+    z.a0 = __builtin_amdgcn_sdot4(m0, zv.x, z.a0, false);
+    z.a1 = __builtin_amdgcn_sdot4(m1, zv.y, z.a1, false);
+    z.a2 = __builtin_amdgcn_sdot4(m2, zv.z, z.a2, false);
+    z.a3 = __builtin_amdgcn_sdot4(m3, zv.w, z.a3, false);
+  }
+};
+
+// LDS byte offset of 16-byte piece p of the activation codes.  The four
+// pieces of 64-weight chunk c are rotated by (c / 2) % 4, so the eight lanes
+// of a ds_read_b128 phase (consecutive chunks, same piece) hit eight
+// different 16-byte bank groups.
+__device__ __forceinline__ int xslot(int p) {
+  const int c = p >> 2;
+  return 16 * (4 * c + ((p & 3) ^ ((c >> 1) & 3)));
+}
+
 // Sum of q over the set bits of 1-bit packed words (binary weights): word w
 // holds 32 weights, weight 4s + b at bit 8b + s, against the activation codes
 // x[0..7] (dword s = the codes of weights 4s .. 4s+3).  Bit s of every byte

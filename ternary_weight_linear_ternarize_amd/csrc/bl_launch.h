@@ -13,6 +13,20 @@ namespace bl {
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp,
                        float* w_scale, uint64_t* bins, hipStream_t s);
 
+// BitNet a4.8 split activations (a48.hip): per row the n_out largest |x|
+// as int8 codes (q8, scale g8), the rest as 4-bit codes in int8 storage (q4,
+// scale g4); both [M][Kp], each zero where the other holds the entry.
+hipError_t launch_act_quant_a48(const void* X, bool bf16, int64_t M, int64_t K, int64_t n_out,
+                                int8_t* q4, float* g4, int32_t* rs4, int8_t* q8, float* g8,
+                                int32_t* rs8, hipStream_t s);
+// Y = (acc4 (g_w g4)) / 7 + (acc8 (g_w g8)) / 127.  acc ([2][M][N] int32:
+// acc4 then acc8) is optional for one token with Kp <= 16384 and required
+// otherwise (the accumulators of the two products are kept there).
+hipError_t launch_forward_a48(const int8_t* x4, const float* g4, const int32_t* rs4,
+                              const int8_t* x8, const float* g8, const int32_t* rs8, int64_t M,
+                              int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N,
+                              float* Y, int32_t* acc, hipStream_t s);
+
 // Y = dequant(Xq . T^T) for binary weights in the 1-bit layout (rows of
 // Kb = K rounded up to 128 weights; Xq rows of Kp = K rounded up to 64):
 // the bit GEMV for one token, the 1-bit MFMA kernel otherwise (bin1.hip).

@@ -89,15 +89,6 @@ __device__ __forceinline__ void gemv_load_w(const GemvArgs& a, int64_t rb, int l
   }
 }
 
-// LDS byte offset of 16-byte piece p of the activation codes.  The four
-// pieces of 64-weight chunk c are rotated by (c / 2) % 4, so the eight lanes
-// of a ds_read_b128 phase (consecutive chunks, same piece) hit eight
-// different 16-byte bank groups.
-__device__ __forceinline__ int xslot(int p) {
-  const int c = p >> 2;
-  return 16 * (4 * c + ((p & 3) ^ ((c >> 1) & 3)));
-}
-
 // Partial dot products of this lane's chunks (lane, lane + 64, ...) with the
 // codes in LDS.
 template <int KC, int R>

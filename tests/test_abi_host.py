@@ -100,6 +100,20 @@ def test_forward_validation():
     assert f(*a, B.BL_KERNEL_SKINNY, None) == B.BL_ESHAPE  # skinny needs M <= 64
     assert f(*args, 9, None) == B.BL_EINVAL
     assert lib.bitlinear_forward(FAKE, FAKE, FAKE, 1, 64, ODD, FAKE, 16, FAKE, None, None) == B.BL_EALIGN
+    h = lib.bitlinear_quant_act_a48
+    assert h(FAKE, 0, 1, 64, 3, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.BL_EINVAL
+    assert h(FAKE, 0, 1, 64, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.BL_ESHAPE
+    assert h(FAKE, 0, 1, 64, 3, ODD, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.BL_EALIGN
+    f48 = lib.bitlinear_forward_a48
+    n48 = lib.bitlinear_a48_workspace_bytes(2, 16)
+    assert n48 == 2 * 16 * 8
+    a48 = [FAKE] * 6 + [2, 64, FAKE, FAKE, 16, FAKE, FAKE, n48, None]
+    b = list(a48); b[13] = n48 - 1
+    assert f48(*b) == B.BL_EWORKSPACE
+    b = list(a48); b[3] = None
+    assert f48(*b) == B.BL_EINVAL
+    b = list(a48); b[3] = ODD
+    assert f48(*b) == B.BL_EALIGN
     g = lib.bitlinear_forward_1bit
     assert g(FAKE, FAKE, None, 1, 64, FAKE, FAKE, 16, FAKE, None, None) == B.BL_EINVAL
     assert g(FAKE, FAKE, FAKE, 0, 64, FAKE, FAKE, 16, FAKE, None, None) == B.BL_ESHAPE

@@ -372,3 +372,56 @@ def test_decode_100b_binary_1bit_full():
     for M in (1, 8):
         q, gx, rs, Xq, xs, xr = check_quant(d["X"][:M])
         check_forward1(q, gx, t, g, Xq, xs, xr, Wb, sc)
+
+
+# ----------------------------------------------------------------------------
+# BitNet a4.8 split activations (int8 outliers + int4 rest)
+
+def check_a48(X, n_out, t, g, Wp, sc, bf16=False):
+    xd = to_dev(X)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        X = xd.float().cpu().numpy()
+    M, K = X.shape
+    N = t.shape[0]
+    ref = oracle.bitlinear_a48(X, t, g, n_out)
+    q = B.bitlinear_quant_act_a48(xd, n_out)
+    h = {k: host(v) for k, v in q.items()}
+    for part in ("q4", "q8"):
+        np.testing.assert_array_equal(h[part][:, :K], ref[part], err_msg=part)
+        assert not h[part][:, K:].any()
+    for part in ("g4", "g8"):
+        np.testing.assert_array_equal(h[part].view(np.uint32), ref[part].view(np.uint32), err_msg=part)
+    np.testing.assert_array_equal(h["rs4"], ref["rs4"])
+    np.testing.assert_array_equal(h["rs8"], ref["rs8"])
+    Y, ws = B.bitlinear_forward_a48(q, K, Wp, sc, N)
+    acc = host(ws)[:2 * M * N].reshape(2, M, N)
+    np.testing.assert_array_equal(acc[0], ref["acc4"])
+    np.testing.assert_array_equal(acc[1], ref["acc8"])
+    assert_rel(host(Y), ref["y"])
+    Y2, _ = B.bitlinear_forward_a48(q, K, Wp, sc, N)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K,N,n_out,bf16", [
+    (1, 2560, 6912, 26, False), (1, 6912, 2560, 69, True), (1, 8192, 300, 82, False),
+    (1, 100, 40, 0, False), (1, 100, 40, 100, False), (1, 100, 40, 1000, False),
+    (1, 16448, 33, 165, False), (3, 700, 130, 7, False), (16, 512, 400, 5, False),
+    (64, 2560, 96, 26, True), (100, 1040, 257, 10, False), (1, 40000, 9, 400, False),
+    (2, 20000, 17, 200, False),
+])
+def test_a48_quant_and_forward(M, K, N, n_out, bf16):
+    d = synth.random_case(5000 + K + N + M, M, K, N)
+    X = synth.with_outliers(d["X"], synth.outlier_columns(5000 + K, K)) if K > 100 else d["X"]
+    if M > 1:
+        X[1] = np.round(X[1] * 2) / 2  # ties in |x| across the threshold
+    g, t, Wp, sc = check_pack(d["W"])
+    check_a48(X, n_out, t, g, Wp, sc, bf16)
+
+
+def test_a48_decode_100b_full():
+    d = synth.decode_100b()
+    g, t, Wp, sc = check_pack(d["W"])
+    del d["W"]
+    for M in (1, 8):
+        check_a48(d["X"][:M], 82, t, g, Wp, sc)
