@@ -81,6 +81,17 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* x_scale, const int3
                               const uint32_t* Wu, const float* su, int64_t N, float* H,
                               float* gh_parts, int* nparts, hipStream_t s);
 
+// Up to 16 tokens with the weights loaded straight into MFMA operands
+// (skinny.hip); direct_ok says whether the shape is covered (LDS, registers).
+bool direct_ok(int64_t M, int64_t K, int64_t N, int nb);
+hipError_t launch_direct(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,
+                         int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
+                         int32_t* acc_out, hipStream_t s);
+hipError_t launch_direct_gateup(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
+                                int64_t M, int64_t K, const uint32_t* Wg, const float* sg,
+                                const uint32_t* Wu, const float* su, int64_t N, float* H,
+                                float* gh_parts, int* nparts, hipStream_t s);
+
 // Split-K skinny GEMM for 1 <= M <= 64 (splitk.hip): grid = ntb weight-row
 // blocks x ksb K parts; with ksb > 1 the int32 partial sums go to `part`
 // (part_elems int32) and a second kernel adds them and dequantises.  ok is

@@ -519,6 +519,7 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
   if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
+  if (direct_ok(M, K, N, 1)) return launch_direct(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   if (stream_ok(M, Kp))
     return stream_launch<1, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
                                       nullptr, nullptr, s);
@@ -545,6 +546,8 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
                               hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
+  if (direct_ok(M, K, N, 2))
+    return launch_direct_gateup(Xq, xs, rs, M, K, Wg, sg, Wu, su, N, H, gh_parts, nparts, s);
   if (stream_ok(M, Kp))
     return stream_launch<2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr, gh_parts,
                                        nparts, s);

@@ -70,8 +70,8 @@ struct TiledGemm {
   static constexpr int LDS = 2 * ABYTES + 8 * BM;
 };
 
-template <int TM, int TN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(256, 2) void tiled_gemm_kernel(
+template <int TM, int TN, int WAVES_M, int WAVES_N, int MINB = 2>
+__global__ __launch_bounds__(256, MINB) void tiled_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp, const uint32_t* __restrict__ W,
     const float* __restrict__ w_scale, int64_t N, float* __restrict__ Y,
