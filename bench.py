@@ -35,8 +35,8 @@ if ROOT not in sys.path:
 # factors a plain 256 MiB copy reads back).  Valid for this kernel build
 # only: set to None whenever the kernel changes until the counters are
 # taken again.
-UP_GEMV_KERNEL = "gemv_kernel<1,4,0,1>"
-UP_GEMV_TRAFFIC_BYTES = 4_661_000
+UP_GEMV_KERNEL = "gemv_kernel<1,4,0,1,512>"
+UP_GEMV_TRAFFIC_BYTES = None
 
 METRIC = ("BitLinear W1.58A8: decode GEMV weight GB/s (% HBM peak); "
           "prefill int8 TOPS (% MFMA)")

@@ -36,18 +36,27 @@ enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3 };
 
 constexpr int kFusedMaxKp = 7168;  // largest padded K quantised inside the GEMV
 
-__device__ __forceinline__ float block_max4(float v, float* red) {
+// Block maximum (non-negative values) / sum over NW waves; red holds NW slots.
+template <int NW>
+__device__ __forceinline__ float block_maxw(float v, float* red) {
   v = dpp::max_nonneg_f32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w]);
+  return r;
 }
 
-__device__ __forceinline__ int block_sum4(int v, int* red) {
+template <int NW>
+__device__ __forceinline__ int block_sumw(int v, int* red) {
   v = dpp::sum_i32(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+  int r = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r += red[w];
+  return r;
 }
 
 struct GemvArgs {
@@ -174,42 +183,44 @@ __device__ __forceinline__ float gemv_epilogue(const GemvArgs& a, int64_t rb, in
 // KC: 64-weight chunks per lane (Kp <= 4096 * KC).  R: weight rows per wave
 // (one row block per wave: every load of the grid is in flight at once, the
 // pattern that measured fastest for both small and large matrices).
-template <int KC, int R, int EPI, int XSRC>
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
+template <int KC, int R, int EPI, int XSRC, int NT>
+__global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;  // output rows per wave
   constexpr bool FUSED = XSRC != XS_INT8;
+  constexpr int NW = NT / 64;  // waves per block
   __shared__ __attribute__((aligned(16))) int8_t xq_lds[4096 * KC];
-  __shared__ float redf[4];
-  __shared__ int redi[4];
+  __shared__ float redf[NW];
+  __shared__ int redi[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int C = (int)(a.Kp >> 6);  // 64-weight chunks per row
   const int wpr = (int)(a.Kp >> 4);
-  const int64_t rb = (int64_t)blockIdx.x * 4 + wave;  // this wave's row block
+  const int64_t rb = (int64_t)blockIdx.x * NW + wave;  // this wave's row block
 
   // Activation loads are issued before the weight loads: vmcnt counts in
   // order, so waiting for the activations then leaves the weights in flight
   // and the staging/quantisation below overlaps the weight stream.
-  constexpr int NWT = 4 * KC;  // fused: words per thread (Kp <= 4096 * KC)
-  int4 xi[KC];
+  constexpr int NWT = 1024 * KC / NT;  // fused: words per thread (Kp <= 4096 * KC)
+  constexpr int NXI = (256 * KC + NT - 1) / NT;  // int8: 16-byte pieces per thread
+  int4 xi[NXI];
   float xv[NWT][4];
   float g = 0.0f;
   if constexpr (!FUSED) {
     const int4* xg = reinterpret_cast<const int4*>(a.x);
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int p = tid + 256 * j;
+    for (int j = 0; j < NXI; ++j) {
+      const int p = tid + NT * j;
       xi[j] = p < 4 * C ? xg[p] : make_int4(0, 0, 0, 0);
     }
   } else {
     const int K = (int)a.K, nw = (int)(a.Kp >> 2);
     if constexpr (XSRC == XS_PARTS) {
-      for (int p = tid; p < a.nparts; p += 256) g = fmaxf(g, a.gparts[p]);
+      for (int p = tid; p < a.nparts; p += NT) g = fmaxf(g, a.gparts[p]);
     }
     const bool vec = (reinterpret_cast<uintptr_t>(a.x) & (XSRC == XS_BF16 ? 7 : 15)) == 0;
 #pragma unroll
     for (int j = 0; j < NWT; ++j) {
-      const int wd = tid + 256 * j;
+      const int wd = tid + NT * j;
       if (vec && 4 * wd + 3 < K) {
         if constexpr (XSRC == XS_BF16) {
           const uint2 u = reinterpret_cast<const uint2*>(a.x)[wd];
@@ -242,8 +253,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
     gx = a.x_scale[0];
     rsum = a.rowsum[0];
 #pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int p = tid + 256 * j;
+    for (int j = 0; j < NXI; ++j) {
+      const int p = tid + NT * j;
       if (p < 4 * C) *reinterpret_cast<int4*>(xq_lds + xslot(p)) = xi[j];
     }
     __syncthreads();
@@ -256,12 +267,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) g = fmaxf(g, fabsf(xv[j][b]));
     }
-    g = block_max4(g, redf);
+    g = block_maxw<NW>(g, redf);
     const QuantDiv qd = make_qdiv(g);
     int rs = 0;
 #pragma unroll
     for (int j = 0; j < NWT; ++j) {
-      const int wd = tid + 256 * j;
+      const int wd = tid + NT * j;
       if (wd < nw) {
         uint32_t pk = 0u;
 #pragma unroll
@@ -274,7 +285,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
         if (blockIdx.x == 0 && a.xq_out) reinterpret_cast<uint32_t*>(a.xq_out)[wd] = pk;
       }
     }
-    rsum = block_sum4(rs, redi);  // its barrier also publishes xq_lds
+    rsum = block_sumw<NW>(rs, redi);  // its barrier also publishes xq_lds
     gx = g;
     if (blockIdx.x == 0 && tid == 0) {
       if (a.xs_out) a.xs_out[0] = g;
@@ -288,11 +299,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   if (rb * RW < a.N) hmax = gemv_epilogue<R, EPI>(a, rb, part, rsum, gx, sw0, sw1);
 
   if constexpr (EPI == EPI_GATEUP) {
-    hmax = dpp::max_nonneg_f32(hmax);
-    __shared__ float redh[4];
-    if (lane == 0) redh[wave] = hmax;
-    __syncthreads();
-    if (tid == 0) a.gh_parts[blockIdx.x] = fmaxf(fmaxf(redh[0], redh[1]), fmaxf(redh[2], redh[3]));
+    __shared__ float redh[NW];
+    hmax = block_maxw<NW>(hmax, redh);
+    if (tid == 0) a.gh_parts[blockIdx.x] = hmax;
   }
 }
 
@@ -345,19 +354,21 @@ __global__ __launch_bounds__(256) void gemv_long_kernel(const GemvArgs a) {
   if (rb * R < a.N) gemv_epilogue<R, EPI_STORE>(a, rb, total, rsum, gx, a.s0[0], 0.0f);
 }
 
-template <int R, int EPI, int XSRC>
-static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s) {
+template <int R, int EPI, int XSRC, int NT = 256>
+static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s, int* nblocks = nullptr) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;
   const int64_t C = a.Kp / 64;
   const int64_t nrb = (a.N + RW - 1) / RW;
-  const unsigned blocks = (unsigned)((nrb + 3) / 4);
   if (C > 256) {
     if (XSRC != XS_INT8 || EPI != EPI_STORE) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemv_long_kernel<R>), dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_long_kernel<R>), dim3((unsigned)((nrb + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
+  constexpr int NW = NT / 64;
+  const unsigned blocks = (unsigned)((nrb + NW - 1) / NW);
+  if (nblocks) *nblocks = (int)blocks;
 #define BL_GEMV_CASE(KCV) \
-  hipLaunchKernelGGL((gemv_kernel<KCV, R, EPI, XSRC>), dim3(blocks), dim3(256), 0, s, a)
+  hipLaunchKernelGGL((gemv_kernel<KCV, R, EPI, XSRC, NT>), dim3(blocks), dim3(NT), 0, s, a)
   if (C <= 64) BL_GEMV_CASE(1);
   else if (C <= 128) BL_GEMV_CASE(2);
   else if (C <= 192) BL_GEMV_CASE(3);
@@ -388,6 +399,8 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, const int32_t* rs, int
   return gemv_dispatch<4, EPI_STORE, XS_INT8>(a, s);
 }
 
+constexpr int64_t kWideGemvBlocks = 192;  // 512-thread blocks at least this many
+
 // The fused kernels redo the row's quantisation in every block; past ~7K
 // inputs that redundant work costs more than a separate quantisation launch.
 bool gemv_fused_ok(int64_t K) { return (K + 63) / 64 * 64 <= kFusedMaxKp; }
@@ -401,6 +414,13 @@ hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t
   a.xq_out = xq_out;
   a.xs_out = xs_out;
   a.rs_out = rs_out;
+  // 8 waves per block halve the blocks that each redo the quantisation (2560
+  // -> 6912: 3.98 -> 3.58 us) while enough blocks remain to fill the CUs;
+  // layers with fewer rows keep 4 waves per block (6912 -> 2560: 4.58 us
+  // against 5.0 us with 8)
+  if ((N + 31) / 32 >= kWideGemvBlocks)
+    return bf16 ? gemv_dispatch<4, EPI_STORE, XS_BF16, 512>(a, s)
+                : gemv_dispatch<4, EPI_STORE, XS_F32, 512>(a, s);
   return bf16 ? gemv_dispatch<4, EPI_STORE, XS_BF16>(a, s)
               : gemv_dispatch<4, EPI_STORE, XS_F32>(a, s);
 }
