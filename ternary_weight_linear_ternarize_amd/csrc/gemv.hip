@@ -388,6 +388,8 @@ static GemvArgs base_args(int64_t K, const uint32_t* Wp, const float* ws, int64_
   return a;
 }
 
+constexpr int64_t kWideGemvBlocks = 192;  // 512-thread blocks at least this many
+
 hipError_t launch_gemv(const int8_t* xq, const float* xs, const int32_t* rs, int64_t K,
                        const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                        int32_t* acc_out, hipStream_t s) {
@@ -396,10 +398,10 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, const int32_t* rs, int
   a.x_scale = xs;
   a.rowsum = rs;
   a.acc_out = acc_out;
-  return gemv_dispatch<4, EPI_STORE, XS_INT8>(a, s);
+  // 2 rows per wave for layers with few rows (6912 -> 2560: 3.31 -> 3.15 us)
+  if (N >= 4096) return gemv_dispatch<4, EPI_STORE, XS_INT8>(a, s);
+  return gemv_dispatch<2, EPI_STORE, XS_INT8>(a, s);
 }
-
-constexpr int64_t kWideGemvBlocks = 192;  // 512-thread blocks at least this many
 
 // The fused kernels redo the row's quantisation in every block; past ~7K
 // inputs that redundant work costs more than a separate quantisation launch.
@@ -415,14 +417,13 @@ hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t
   a.xs_out = xs_out;
   a.rs_out = rs_out;
   // 8 waves per block halve the blocks that each redo the quantisation (2560
-  // -> 6912: 3.98 -> 3.58 us) while enough blocks remain to fill the CUs;
-  // layers with fewer rows keep 4 waves per block (6912 -> 2560: 4.58 us
-  // against 5.0 us with 8)
+  // -> 6912: 3.98 -> 3.58 us); layers with fewer rows take 2 rows per wave
+  // so that enough blocks remain (6912 -> 2560: 4.63 -> 3.85 us)
   if ((N + 31) / 32 >= kWideGemvBlocks)
     return bf16 ? gemv_dispatch<4, EPI_STORE, XS_BF16, 512>(a, s)
                 : gemv_dispatch<4, EPI_STORE, XS_F32, 512>(a, s);
-  return bf16 ? gemv_dispatch<4, EPI_STORE, XS_BF16>(a, s)
-              : gemv_dispatch<4, EPI_STORE, XS_F32>(a, s);
+  return bf16 ? gemv_dispatch<2, EPI_STORE, XS_BF16, 512>(a, s)
+              : gemv_dispatch<2, EPI_STORE, XS_F32, 512>(a, s);
 }
 
 hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, int64_t K,
@@ -435,7 +436,8 @@ hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, in
   a.xq_out = xq_out;
   a.xs_out = xs_out;
   a.rs_out = rs_out;
-  return gemv_dispatch<4, EPI_STORE, XS_PARTS>(a, s);
+  if ((N + 31) / 32 >= kWideGemvBlocks) return gemv_dispatch<4, EPI_STORE, XS_PARTS, 512>(a, s);
+  return gemv_dispatch<2, EPI_STORE, XS_PARTS, 512>(a, s);
 }
 
 constexpr int kGateupR = 4;  // weight rows per wave in the gate/up GEMV (half gate, half up)
