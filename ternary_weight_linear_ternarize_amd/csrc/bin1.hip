@@ -11,9 +11,9 @@
 //  * one token: gemv1_kernel, the GEMV of gemv.hip with 128 weights (one
 //    16-byte load) per lane and chunk; the dot product masks bit s of every
 //    byte in place (DotBits32) and adds 2 * sum - rowsum at the end;
-//  * up to 16 tokens (K <= 8192): mfma1s_kernel, v_mfma_i32_16x16x64_i8 with
-//    the bits expanded to the bytes 0 / 2 by one shift and one mask per 4
-//    weights, every weight load of a wave issued up front;
+//  * up to 16 tokens: the streaming skinny MFMA kernel of gemm.hip in its
+//    1-bit mode (each bit expanded to the byte 2 bit = t + 1 by one shift and
+//    one mask per 4 weights, so its epilogue is the 2-bit one);
 //  * otherwise: mfma1_kernel, the same MFMA with K walked in segments of 1024
 //    whose activations are staged into LDS (double buffered, direct-to-LDS
 //    loads) while the previous segment is computed; batches above 64 tokens
@@ -117,26 +117,11 @@ __global__ __launch_bounds__(256) void gemv1_kernel(const Gemv1Args a) {
   }
 }
 
-// MFMA operand of weights 16h .. 16h+15 of a 1-bit word: dword d holds group
-// s = 4h + d (weights 4s .. 4s+3, bit s of each byte) as the bytes 2 * bit.
-template <int H>
-__device__ __forceinline__ v4i bits_operand(uint32_t w) {
-  v4i r;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const int s = 4 * H + d;
-    r[d] = (int)((s == 0 ? (w << 1) : (w >> (s - 1))) & 0x02020202u);
-  }
-  return r;
-}
-
 constexpr int kB1Lpr = 8;                    // lanes per weight row per load (8 x 16 B)
 constexpr int kB1Seg = kB1Lpr * 128;         // weights per row per step and K segment
 constexpr int kB1Bp = kB1Seg / 8 + 16;       // staged bytes per weight row (+ pad)
 constexpr int kB1Pitch = kB1Seg + 16;        // staged activation row (+16 B spreads banks)
 constexpr int kB1Wpb = 4;                    // waves (16-row weight tiles) per block
-constexpr int kB1WpbS = 8;                   // the same for mfma1s_kernel
-constexpr int64_t kB1LdsMax = 160 * 1024;    // dynamic LDS limit of mfma1s_kernel (all of it)
 
 __host__ __device__ constexpr int64_t b1_xbuf_bytes(int tms) {
   return staged_rows_bytes(16 * tms, kB1Pitch);
@@ -249,121 +234,6 @@ __global__ __launch_bounds__(64 * kB1Wpb) void mfma1_kernel(
     }
 }
 
-// Up to 16 tokens and Kb <= 1024 NS: the whole activation block (M x Kb) is
-// staged into LDS once, and every weight load of a wave (16 rows x Kb bits,
-// row-contiguous 16-byte lanes) is issued up front into registers -- half
-// the registers the 2-bit codes would need.  The activations go through
-// registers (XR 16-byte pieces per thread, loaded before the weights), so the
-// block waits only for them before its barrier and each step then waits for
-// its own weights (vmcnt counts in order): later steps stream in while the
-// first ones are computed.  Every load is branch-free (clamped addresses,
-// out-of-range data zeroed when staged).
-template <int NS, int XR>
-__global__ __launch_bounds__(64 * kB1WpbS) void mfma1s_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ rowsum, int M, int64_t Kp, int64_t Kb,
-    const uint32_t* __restrict__ W, const float* __restrict__ w_scale, int64_t N,
-    float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-  constexpr int RPI = 64 / kB1Lpr;
-  constexpr int NI = 16 / RPI;
-  constexpr int NT = 64 * kB1WpbS;
-  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, li = lane & 15;
-  const int nsteps = (int)((Kb + kB1Seg - 1) / kB1Seg);  // <= NS
-  const int pitch = nsteps * kB1Seg + 16;  // whole steps: reads past Kb stay in the row
-  const int xrows = M < 16 ? M + 1 : 16;   // row M (if any) stays zero: the MFMA rows past M
-  int8_t* lds_x = lds;
-  int8_t* lds_w = lds + (int64_t)xrows * pitch + wave * 16 * kB1Bp;
-  const int64_t wpr = Kb / 32;
-  const int C = (int)(Kb / 128);
-  const int64_t nbase = (int64_t)blockIdx.x * (16 * kB1WpbS) + 16 * wave;
-  const int lr = lane / kB1Lpr, lc = lane % kB1Lpr;
-
-  // activation pieces: staged row r, piece col < ppr; codes for r < M, col < kpp
-  const int ppr = pitch / 16, kpp = (int)(Kp / 16), total = xrows * ppr;
-  uint4 xr[XR];
-#pragma unroll
-  for (int j = 0; j < XR; ++j) {
-    int pc = tid + NT * j;
-    pc = pc < total ? pc : total - 1;
-    int row = pc / ppr;
-    int col = pc - row * ppr;
-    row = row < M ? row : M - 1;
-    col = col < kpp ? col : kpp - 1;
-    xr[j] = *reinterpret_cast<const uint4*>(Xq + (int64_t)row * Kp + 16 * col);
-  }
-  uint4 st[NS][NI];
-#pragma unroll
-  for (int sp = 0; sp < NS; ++sp)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      int64_t n = nbase + RPI * i + lr;
-      n = n < N ? n : N - 1;
-      int c = sp * kB1Lpr + lc;
-      c = c < C ? c : C - 1;
-      st[sp][i] = load_stream_u4(reinterpret_cast<const uint4*>(W + n * wpr) + c);
-    }
-  // straight-line stores (a conditional one would pull its load after the
-  // weight loads): threads past the end rewrite the last piece, same value
-#pragma unroll
-  for (int j = 0; j < XR; ++j) {
-    int pc = tid + NT * j;
-    pc = pc < total ? pc : total - 1;
-    const int row = pc / ppr, col = pc - row * ppr;
-    *reinterpret_cast<uint4*>(lds_x + row * pitch + 16 * col) =
-        (row < M && col < kpp) ? xr[j] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  __syncthreads();
-
-  v4i acc[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-  // token rows past M read the zero row: no branch around the operand reads
-  const int8_t* xrow = lds_x + (li < M ? li : xrows - 1) * pitch + 64 * g;
-  const int8_t* wrow = lds_w + li * kB1Bp + 8 * g;
-#pragma unroll
-  for (int sp = 0; sp < NS; ++sp) {
-    if (sp < nsteps) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const bool ok = sp * kB1Lpr + lc < C;  // past the row: zero weights
-        *reinterpret_cast<uint4*>(lds_w + (RPI * i + lr) * kB1Bp + 16 * lc) =
-            ok ? st[sp][i] : make_uint4(0u, 0u, 0u, 0u);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // every 256-weight block of the step (weights past Kb are zero)
-      const int8_t* xs0 = xrow + sp * kB1Seg;
-#pragma unroll
-      for (int blk = 0; blk < kB1Seg / 256; ++blk) {
-        const uint2 bw = *reinterpret_cast<const uint2*>(wrow + 32 * blk);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t wd = s < 2 ? bw.x : bw.y;
-          const v4i bv = (s & 1) ? bits_operand<1>(wd) : bits_operand<0>(wd);
-          const v4i av = *reinterpret_cast<const v4i*>(xs0 + 256 * blk + 16 * s);
-          acc[s & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, acc[s & 1], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-
-  const int64_t n = nbase + li;
-  const float sw = w_scale[0];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = 4 * g + r;
-    if (m < M && n < N) {
-      const int a = acc[0][r] + acc[1][r] - rowsum[m];
-      Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
-      if (acc_out) acc_out[(int64_t)m * N + n] = a;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -389,45 +259,6 @@ static hipError_t mfma1_go(const int8_t* Xq, const float* xs, const int32_t* rs,
   return hipGetLastError();
 }
 
-// LDS of mfma1s_kernel: the staged rows (M, plus a zero row when M < 16) of
-// whole steps, and the waves' weight patches.
-static int64_t mfma1s_lds(int64_t M, int64_t Kb) {
-  const int64_t pitch = (Kb + kB1Seg - 1) / kB1Seg * kB1Seg + 16;
-  return (M < 16 ? M + 1 : 16) * pitch + (int64_t)kB1WpbS * 16 * kB1Bp;
-}
-
-template <int NS, int XR>
-static hipError_t mfma1s_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
-                            int64_t Kp, int64_t Kb, const uint32_t* Wb, const float* ws, int64_t N,
-                            float* Y, int32_t* acc_out, hipStream_t s) {
-  auto kern = mfma1s_kernel<NS, XR>;
-  static bool once = ((void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                (int)kB1LdsMax),
-                      true);
-  (void)once;
-  const int64_t lds = mfma1s_lds(M, Kb);
-  const unsigned blocks = (unsigned)((N + 16 * kB1WpbS - 1) / (16 * kB1WpbS));
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * kB1WpbS), (size_t)lds, s, Xq, xs, rs, (int)M,
-                     Kp, Kb, Wb, ws, N, Y, acc_out);
-  return hipGetLastError();
-}
-
-// mfma1s_kernel covers M <= 16 with Kb <= 8192 (its LDS then fits).
-static bool mfma1s_ok(int64_t M, int64_t Kb) {
-  return M <= 16 && Kb <= 8 * kB1Seg && mfma1s_lds(M, Kb) <= kB1LdsMax;
-}
-
-template <int XR>
-static hipError_t mfma1s_ns(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
-                            int64_t Kp, int64_t Kb, const uint32_t* Wb, const float* ws, int64_t N,
-                            float* Y, int32_t* acc_out, hipStream_t s) {
-  const int64_t ns = (Kb + kB1Seg - 1) / kB1Seg;
-  if (ns <= 2) return mfma1s_go<2, XR>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-  if (ns <= 4) return mfma1s_go<4, XR>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-  return mfma1s_go<8, XR>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-}
-
 hipError_t launch_forward_1bit(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                                int64_t K, const uint32_t* Wb, const float* ws, int64_t N, float* Y,
                                int32_t* acc_out, hipStream_t s) {
@@ -440,15 +271,7 @@ hipError_t launch_forward_1bit(const int8_t* Xq, const float* xs, const int32_t*
     if (C <= 192) return gemv1_go<3, 2>(a, s);
     return gemv1_go<4, 2>(a, s);
   }
-  if (mfma1s_ok(M, Kb)) {
-    // 16-byte activation pieces per thread (zero row included)
-    const int64_t pitch = (Kb + kB1Seg - 1) / kB1Seg * kB1Seg + 16;
-    const int64_t xr = ((M < 16 ? M + 1 : 16) * (pitch / 16) + 64 * kB1WpbS - 1) / (64 * kB1WpbS);
-    if (xr <= 3) return mfma1s_ns<3>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-    if (xr <= 5) return mfma1s_ns<5>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-    if (xr <= 9) return mfma1s_ns<9>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-    return mfma1s_ns<17>(Xq, xs, rs, M, Kp, Kb, Wb, ws, N, Y, acc_out, s);
-  }
+  if (stream_1bit_ok(M, K)) return launch_stream_1bit(Xq, xs, rs, M, K, Wb, ws, N, Y, acc_out, s);
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int64_t ms = M - m0 < 64 ? M - m0 : 64;
     const int8_t* x = Xq + m0 * Kp;

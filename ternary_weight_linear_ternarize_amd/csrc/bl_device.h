@@ -640,6 +640,19 @@ struct DotBits32 {
   __device__ __forceinline__ int total() const { return a0 + (a1 >> 1) + (a2 >> 2) + (a3 >> 3); }
 };
 
+// MFMA operand of weights 16h .. 16h+15 of a 1-bit word: dword d holds group
+// s = 4h + d (weights 4s .. 4s+3, bit s of each byte) as the bytes 2 * bit.
+template <int H>
+__device__ __forceinline__ v4i bits_operand(uint32_t w) {
+  v4i r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int s = 4 * H + d;
+    r[d] = (int)((s == 0 ? (w << 1) : (w >> (s - 1))) & 0x02020202u);
+  }
+  return r;
+}
+
 // Reduce v[0..R) (per-lane partials of R rows) across the 64 lanes with a
 // transposing butterfly on DPP / lane-swap moves, small strides first: the
 // first log2 R steps exchange halves of the row set, the rest add.  On return

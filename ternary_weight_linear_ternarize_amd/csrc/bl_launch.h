@@ -27,6 +27,13 @@ hipError_t launch_forward_a48(const int8_t* x4, const float* g4, const int32_t* 
                               int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N,
                               float* Y, int32_t* acc, hipStream_t s);
 
+// The streaming skinny MFMA kernel on 1-bit binary weights (M <= 16 while
+// the activations fit its LDS: stream_1bit_ok).
+bool stream_1bit_ok(int64_t M, int64_t K);
+hipError_t launch_stream_1bit(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
+                              int64_t M, int64_t K, const uint32_t* Wb, const float* w_scale,
+                              int64_t N, float* Y, int32_t* acc_out, hipStream_t s);
+
 // Y = dequant(Xq . T^T) for binary weights in the 1-bit layout (rows of
 // Kb = K rounded up to 128 weights; Xq rows of Kp = K rounded up to 64):
 // the bit GEMV for one token, the 1-bit MFMA kernel otherwise (bin1.hip).

@@ -263,17 +263,18 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
 // and the partial accumulators of waves 1 .. KS-1 are added to wave 0's
 // through LDS before the epilogue (more waves in flight for layers with few
 // rows, e.g. the FFN's down projection).
-template <int NB, int LPR, int WPB, int D, int EPI, int KS>
+template <int NB, int LPR, int WPB, int D, int EPI, int KS, int BITS = 2>
 __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ rowsum, int M, int64_t Kp, const uint32_t* __restrict__ W0,
-    const float* __restrict__ s0, const uint32_t* __restrict__ W1, const float* __restrict__ s1,
-    int64_t N, float* __restrict__ Y, int32_t* __restrict__ acc_out,
-    float* __restrict__ gh_parts) {
-  constexpr int STEP = LPR * 64;                 // weights per row per step (16 B per lane)
+    const int32_t* __restrict__ rowsum, int M, int64_t Kp, int64_t Kw,
+    const uint32_t* __restrict__ W0, const float* __restrict__ s0,
+    const uint32_t* __restrict__ W1, const float* __restrict__ s1, int64_t N,
+    float* __restrict__ Y, int32_t* __restrict__ acc_out, float* __restrict__ gh_parts) {
+  static_assert(BITS == 2 || BITS == 1, "2-bit codes or the 1-bit binary layout");
+  constexpr int STEP = LPR * 64 * (2 / BITS);    // weights per row per step (16 B per lane)
   constexpr int RPI = 64 / LPR;                  // rows per load instruction
   constexpr int NI = 16 / RPI;                   // load instructions per matrix per step
-  constexpr int BP = STEP / 4 + 16;              // bytes per staged weight row (+ pad)
+  constexpr int BP = STEP * BITS / 8 + 16;       // bytes per staged weight row (+ pad)
   constexpr int TPB = WPB / KS;                  // 16-row tiles per block
   static_assert(TPB * KS == WPB, "KS divides WPB");
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
@@ -286,9 +287,11 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   const int64_t xbytes = staged_rows_bytes(M, pitch);
   int8_t* lds_w = lds + xbytes + (int64_t)wave * NB * 16 * BP;
   v4i* lds_part = reinterpret_cast<v4i*>(lds + xbytes + (int64_t)WPB * NB * 16 * BP);
-  const int64_t wpr = Kp / 16;
-  const int C = (int)(Kp / 64);                  // 16-byte pieces per row
-  const int nsteps_all = (int)((Kp + STEP - 1) / STEP);
+  // weight rows hold Kw weights (Kp for 2-bit codes, Kp rounded up to 128 for
+  // the 1-bit layout)
+  const int64_t wpr = Kw * BITS / 32;
+  const int C = (int)(Kw * BITS / 128);          // 16-byte pieces per row
+  const int nsteps_all = (int)((Kw + STEP - 1) / STEP);
   const int s_begin = kpart * nsteps_all / KS, s_end = (kpart + 1) * nsteps_all / KS;
   const int nsteps = s_end - s_begin;            // this wave's steps
   const int64_t nbase = (int64_t)blockIdx.x * (16 * TPB) + 16 * tile;  // first row of the tile
@@ -305,8 +308,9 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
         int64_t n = nbase + RPI * i + lr;
         n = n < N ? n : N - 1;
         const int c = (s_begin + sidx) * LPR + lc;
+        constexpr uint32_t kPad = BITS == 2 ? 0x55555555u : 0u;  // zero weights / zero bytes
         dst[mat][i] = c < C ? load_stream_u4(reinterpret_cast<const uint4*>(W + n * wpr) + c)
-                            : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+                            : make_uint4(kPad, kPad, kPad, kPad);
       }
     }
   };
@@ -348,11 +352,20 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     const int64_t k0 = (int64_t)(s_begin + sidx) * STEP;
 #pragma unroll
     for (int b = 0; b < STEP / 256; ++b) {
-      if (k0 + 256 * b < Kp) {
+      if (k0 + 256 * b < Kw) {
+        // this lane's 64 weights of the 256-weight block: 16 bytes of codes
+        // or 8 bytes of bits
         uint4 bw[NB];
 #pragma unroll
-        for (int mat = 0; mat < NB; ++mat)
-          bw[mat] = *reinterpret_cast<const uint4*>(lds_w + (mat * 16 + li) * BP + 64 * b + 16 * g);
+        for (int mat = 0; mat < NB; ++mat) {
+          const int8_t* pw = lds_w + (mat * 16 + li) * BP;
+          if constexpr (BITS == 2) {
+            bw[mat] = *reinterpret_cast<const uint4*>(pw + 64 * b + 16 * g);
+          } else {
+            const uint2 h = *reinterpret_cast<const uint2*>(pw + 32 * b + 8 * g);
+            bw[mat] = make_uint4(h.x, h.y, 0u, 0u);
+          }
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int64_t ka = k0 + 256 * b + 64 * g + 16 * s;  // this lane's activation bytes
@@ -360,9 +373,14 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
           if (arow && ka < Kp) a = *reinterpret_cast<const v4i*>(xrow + k0 + 256 * b + 16 * s);
 #pragma unroll
           for (int mat = 0; mat < NB; ++mat) {
-            const uint32_t wd = s == 0 ? bw[mat].x : s == 1 ? bw[mat].y : s == 2 ? bw[mat].z : bw[mat].w;
-            acc[mat][s & 1] =
-                __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_operand(wd), acc[mat][s & 1], 0, 0, 0);
+            v4i bv;
+            if constexpr (BITS == 2) {
+              bv = unpack_operand(s == 0 ? bw[mat].x : s == 1 ? bw[mat].y : s == 2 ? bw[mat].z : bw[mat].w);
+            } else {
+              const uint32_t wd = s < 2 ? bw[mat].x : bw[mat].y;
+              bv = (s & 1) ? bits_operand<1>(wd) : bits_operand<0>(wd);
+            }
+            acc[mat][s & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bv, acc[mat][s & 1], 0, 0, 0);
           }
         }
       }
@@ -460,38 +478,40 @@ static int64_t stream_lds_bytes(int64_t M, int64_t Kp, int nb, int wpb, int ks) 
          (int64_t)(wpb / ks) * (ks - 1) * nb * 1024;
 }
 
-template <int NB, int WPB, int KS, int EPI>
+template <int NB, int WPB, int KS, int EPI, int BITS>
 static hipError_t stream_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
-                            int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
-                            const float* s1, int64_t N, float* Y, int32_t* acc_out,
-                            float* gh_parts, int* nparts, hipStream_t s) {
+                            int64_t Kp, int64_t Kw, const uint32_t* W0, const float* s0,
+                            const uint32_t* W1, const float* s1, int64_t N, float* Y,
+                            int32_t* acc_out, float* gh_parts, int* nparts, hipStream_t s) {
   constexpr int TPB = WPB / KS;
   const size_t lds = (size_t)stream_lds_bytes(M, Kp, NB, WPB, KS);
   const unsigned blocks = (unsigned)((N + 16 * TPB - 1) / (16 * TPB));
   if (nparts) *nparts = (int)blocks;
   constexpr int D = 1;  // steps of weights in flight (2 and 4 measured slower: VGPR pressure)
-  static bool once = (allow_lds(mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS>), true);
+  static bool once =
+      (allow_lds(mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS>), true);
   (void)once;
-  hipLaunchKernelGGL((mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS>), dim3(blocks),
-                     dim3(64 * WPB), lds, s, Xq, xs, rs, (int)M, Kp, W0, s0, W1, s1, N, Y, acc_out,
-                     gh_parts);
+  hipLaunchKernelGGL((mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS>), dim3(blocks),
+                     dim3(64 * WPB), lds, s, Xq, xs, rs, (int)M, Kp, Kw, W0, s0, W1, s1, N, Y,
+                     acc_out, gh_parts);
   return hipGetLastError();
 }
 
 // Tiles (16 weight rows) per block as keep about 200 blocks, most of the 256
 // CUs busy (more tiles per block share one staged copy of the activations);
 // layers with too few rows for that split K over 2 or 4 waves per tile.
-template <int NB, int EPI>
+template <int NB, int EPI, int BITS = 2>
 static hipError_t stream_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                                 int64_t Kp, const uint32_t* W0, const float* s0,
                                 const uint32_t* W1, const float* s1, int64_t N, float* Y,
                                 int32_t* acc_out, float* gh_parts, int* nparts, hipStream_t s) {
+  const int64_t Kw = BITS == 2 ? Kp : (Kp + 127) / 128 * 128;  // weights per row
   auto fits = [&](int wpb, int ks) { return stream_lds_bytes(M, Kp, NB, wpb, ks) <= kStreamLds; };
   const int64_t tiles = (N + 15) / 16;
-  const int64_t nsteps = (Kp + 64 * kStreamLpr - 1) / (64 * kStreamLpr);
-#define BL_STREAM_GO(WPB, KS)                                                                    \
-  return stream_go<NB, WPB, KS, EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, \
-                                     nparts, s)
+  const int64_t nsteps = (Kw + 64 * kStreamLpr * (2 / BITS) - 1) / (64 * kStreamLpr * (2 / BITS));
+#define BL_STREAM_GO(WPB, KS)                                                                 \
+  return stream_go<NB, WPB, KS, EPI, BITS>(Xq, xs, rs, M, Kp, Kw, W0, s0, W1, s1, N, Y,       \
+                                           acc_out, gh_parts, nparts, s)
   if (tiles >= 200 * 8 && fits(8, 1)) BL_STREAM_GO(8, 1);
   if (tiles >= 200 * 4 && fits(4, 1)) BL_STREAM_GO(4, 1);
   if (tiles >= 200 * 2 && fits(2, 1)) BL_STREAM_GO(2, 1);
@@ -536,6 +556,16 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                                              acc_out, nullptr, nullptr, s);
   return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                            acc_out, nullptr, nullptr, s);
+}
+
+bool stream_1bit_ok(int64_t M, int64_t K) { return stream_ok(M, (K + 63) / 64 * 64); }
+
+hipError_t launch_stream_1bit(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                              int64_t K, const uint32_t* Wb, const float* ws, int64_t N, float* Y,
+                              int32_t* acc_out, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  return stream_launch<1, MF_STORE, 1>(Xq, xs, rs, M, Kp, Wb, ws, nullptr, nullptr, N, Y, acc_out,
+                                       nullptr, nullptr, s);
 }
 
 int64_t mfma_gateup_parts(int64_t M, int64_t N) {
