@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 # only: set to None whenever the kernel changes until the counters are
 # taken again.
 UP_GEMV_KERNEL = "gemv_kernel<1,4,0,1,512>"
-UP_GEMV_TRAFFIC_BYTES = None
+UP_GEMV_TRAFFIC_BYTES = 4632322
 
 METRIC = ("BitLinear W1.58A8: decode GEMV weight GB/s (% HBM peak); "
           "prefill int8 TOPS (% MFMA)")
