@@ -120,6 +120,7 @@ def test_single_layer_512_to_400_all_kernels():
     (1, 1, 1), (1, 15, 17), (1, 63, 257), (1, 65, 400), (1, 1040, 33), (1, 4160, 70), (1, 16448, 9),
     (2, 64, 16), (3, 16, 63), (5, 65, 64), (8, 1040, 257), (16, 512, 400), (17, 63, 15),
     (31, 1000, 100), (33, 129, 65), (64, 2560, 96), (65, 300, 130), (100, 1040, 257), (129, 64, 129),
+    (300, 700, 600),
 ])
 def test_random_ragged_shapes(M, K, N):
     d = synth.random_case(1000 + M * 7 + N, M, K, N)
