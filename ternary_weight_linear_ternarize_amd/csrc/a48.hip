@@ -12,9 +12,9 @@
 //   y = (acc4 * (g_w g4)) / 7 + (acc8 * (g_w g8)) / 127.
 //
 //  * a48_quant_kernel: one block per row; the n_out-th largest |x| is found by
-//    an MSB-first radix select on the bits of |x| (4 passes of 8 bits, LDS
-//    histograms), ties at the threshold are taken in index order through a
-//    block prefix count;
+//    an MSB-first radix select on the bits of |x| (digits of 12, 12 and 7
+//    bits, LDS histograms), ties at the threshold are taken in index order
+//    through a block prefix count;
 //  * gemv_a48_kernel (one token): the GEMV of gemv.hip with both code
 //    vectors in LDS and the masked weight fields shared by the two dot
 //    products (Dot16x2);
@@ -50,28 +50,16 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   return base + inc - v;
 }
 
-template <int NT>
-__device__ float block_max_nonneg(float v, float* sh) {
-  v = dpp::max_nonneg_f32(v);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) r = fmaxf(r, sh[w]);
-  __syncthreads();
-  return r;
-}
-
-template <int NT>
-__device__ int block_sum(int v, int* sh) {
-  v = dpp::sum_i32(v);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int r = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) r += sh[w];
-  __syncthreads();
-  return r;
+// Inclusive prefix sum over the 64 lanes of a wave (row shifts within rows
+// of 16 lanes, then the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp::mov<0x111>(0, x);
+  x += dpp::mov<0x112>(0, x);
+  x += dpp::mov<0x114>(0, x);
+  x += dpp::mov<0x118>(0, x);
+  x += dpp::mov<dpp::kBcast15, 0xA>(0, x);
+  x += dpp::mov<dpp::kBcast31, 0xC>(0, x);
+  return x;
 }
 
 __device__ __forceinline__ int a48_code(float x, float q, float d) {
@@ -81,6 +69,16 @@ __device__ __forceinline__ int a48_code(float x, float q, float d) {
 }
 
 // Thread t owns indices t E .. t E + E - 1 (index order = thread order).
+//
+// The n_out-th largest key T (key = the bits of |x|, bit 31 clear) is found
+// digit by digit, bits 30..19, 18..7 and 6..0: every thread adds its
+// keys that match the digits found so far to an LDS histogram of the next
+// digit; wave 0 then scans that histogram from the top (each lane sums a run
+// of bins, a wave prefix sum picks the run, its lane walks it) while the
+// other waves clear the histogram the next digit uses.  Two barriers per
+// digit.  Keys equal to T are outliers in index order up to the number still
+// needed; the block prefix count that ranks them runs only when the keys
+// equal to T are more than that.
 template <bool BF16, int E>
 __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict__ X, int64_t K,
                                                          int64_t Kp, int n_out,
@@ -90,12 +88,13 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
                                                          int8_t* __restrict__ Xq8,
                                                          float* __restrict__ g8o,
                                                          int32_t* __restrict__ rs8o) {
-  constexpr int NT = 1024;
-  __shared__ int hist[256];
-  __shared__ int shi[NT / 64];
-  __shared__ float shf[NT / 64];
-  __shared__ int sel[2];
-  const int tid = threadIdx.x;
+  constexpr int NT = 1024, NW = NT / 64, HB = 4096;
+  __shared__ __attribute__((aligned(16))) int hist[2][HB];
+  __shared__ int shi[2][NW];
+  __shared__ float shf[2][NW];
+  __shared__ int sel[3];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t m = blockIdx.x;
   const int64_t k0 = (int64_t)tid * E;
   const char* row = reinterpret_cast<const char*>(X) + m * K * (BF16 ? 2 : 4);
@@ -105,33 +104,61 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
   for (int e = 0; e < E; ++e) v[e] = (k0 + e < K) ? load_act<BF16>(row, k0 + e) : 0.0f;
   auto key = [&](int e) { return __float_as_uint(v[e]) & 0x7fffffffu; };
 
-  // radix select: T = the n_out-th largest key, need = how many keys equal
-  // to T are outliers
   const int nsel = n_out < K ? n_out : (int)K;
   uint32_t T = 0u, pmask = 0u;
-  int need = nsel;
+  int need = nsel, nties = 0;
   if (nsel > 0 && nsel < K) {
-#pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
+    for (int i = tid; i < 2 * HB; i += NT) (&hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int shift = p == 0 ? 19 : p == 1 ? 7 : 0;
+      const int nb = p == 2 ? 128 : 4096;
+      int* h = hist[p & 1];
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (k0 + e < K && (key(e) & pmask) == T) atomicAdd(&hist[(key(e) >> shift) & 255u], 1);
+        if (k0 + e < K && (key(e) & pmask) == T)
+          atomicAdd(&h[(key(e) >> shift) & (uint32_t)(nb - 1)], 1);
       __syncthreads();
-      // digits from the top: exclusive prefix = count of keys in higher bins
-      const int hv = tid < 256 ? hist[255 - tid] : 0;
-      int tot;
-      const int above = block_excl_scan<NT>(hv, shi, &tot);
-      if (tid < 256 && above < need && above + hv >= need) {
-        sel[0] = 255 - tid;
-        sel[1] = above;
+      if (wave == 0) {
+        // lane l sums bins nb-1-l*per down to nb-(l+1)*per; a wave prefix sum
+        // picks the lane whose run holds the need-th key from the top, then
+        // that run is spread over the lanes (one bin each) and scanned again
+        const int per = nb / 64;
+        const int lo = nb - (lane + 1) * per;
+        int run = 0;
+        if (per >= 4) {
+          const int4* hp = reinterpret_cast<const int4*>(h + lo);
+          for (int j = 0; j < per / 4; ++j) {
+            const int4 q = hp[j];
+            run += q.x + q.y + q.z + q.w;
+          }
+        } else {
+          for (int j = 0; j < per; ++j) run += h[lo + j];
+        }
+        const int inc = wave_incl_scan(run);
+        const uint64_t hit = __ballot(inc - run < need && need <= inc);
+        const int L = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+        const int base = __builtin_amdgcn_readlane(inc - run, L);
+        const int top = nb - 1 - L * per;
+        const int c = lane < per ? h[top - lane] : 0;
+        const int inc2 = wave_incl_scan(c) + base;
+        const uint64_t hit2 = __ballot(inc2 - c < need && need <= inc2);
+        const int J = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit2));
+        if (lane == J) {
+          sel[0] = top - J;
+          sel[1] = inc2 - c;
+          sel[2] = c;
+        }
+      } else if (p == 1) {
+        // the last digit counts into hist[0] again
+        for (int i = tid - 64; i < HB; i += NT - 64) hist[0][i] = 0;
       }
       __syncthreads();
       T |= (uint32_t)sel[0] << shift;
-      pmask |= 0xffu << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
       need -= sel[1];
-      __syncthreads();
+      nties = sel[2];
     }
   }
 
@@ -142,12 +169,16 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
   } else if (nsel == 0) {
 #pragma unroll
     for (int e = 0; e < E; ++e) out[e] = false;
+  } else if (nties == need) {
+    // every key equal to T is an outlier
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[e] = k0 + e < K && key(e) >= T;
   } else {
     int eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) eq += (k0 + e < K && key(e) == T) ? 1 : 0;
     int tot;
-    int r = block_excl_scan<NT>(eq, shi, &tot);  // rank of this thread's first tie
+    int r = block_excl_scan<NT>(eq, &shi[0][0], &tot);  // rank of this thread's first tie
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const bool real = k0 + e < K;
@@ -157,6 +188,7 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
     }
   }
 
+  // both scales in one block reduction
   float a8 = 0.0f, a4 = 0.0f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -164,8 +196,18 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
     if (out[e]) a8 = fmaxf(a8, a);
     else a4 = fmaxf(a4, a);
   }
-  a8 = block_max_nonneg<NT>(a8, shf);
-  a4 = block_max_nonneg<NT>(a4, shf);
+  a8 = dpp::max_nonneg_f32(a8);
+  a4 = dpp::max_nonneg_f32(a4);
+  if (lane == 0) {
+    shf[0][wave] = a8;
+    shf[1][wave] = a4;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    a8 = fmaxf(a8, shf[0][w]);
+    a4 = fmaxf(a4, shf[1][w]);
+  }
   const float d8 = __fadd_rn(a8, kEps), d4 = __fadd_rn(a4, kEps);
 
   int s4 = 0, s8 = 0;
@@ -192,13 +234,25 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
       *reinterpret_cast<uint32_t*>(Xq8 + m * Kp + k) = w8[j];
     }
   }
-  s4 = block_sum<NT>(s4, shi);
-  s8 = block_sum<NT>(s8, shi);
+  // both row sums in one block reduction (shi[1] is not in use by the tie scan)
+  s4 = dpp::sum_i32(s4);
+  s8 = dpp::sum_i32(s8);
+  if (lane == 0) {
+    shi[0][wave] = s4;
+    shi[1][wave] = s8;
+  }
+  __syncthreads();
   if (tid == 0) {
+    int t4 = 0, t8 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      t4 += shi[0][w];
+      t8 += shi[1][w];
+    }
     g4o[m] = a4;
     g8o[m] = a8;
-    rs4o[m] = s4;
-    rs8o[m] = s8;
+    rs4o[m] = t4;
+    rs8o[m] = t8;
   }
 }
 

@@ -426,3 +426,16 @@ def test_a48_decode_100b_full():
     del d["W"]
     for M in (1, 8):
         check_a48(d["X"][:M], 82, t, g, Wp, sc)
+
+
+@pytest.mark.parametrize("K", [3000, 5000])
+def test_a48_quant_degenerate_rows(K):
+    # rows made of ties: all equal, zeros, a block of equal maxima, few distinct values
+    X = np.zeros((4, K), np.float32)
+    X[1] = 1.5
+    X[2, ::3] = -2.0
+    X[3] = np.tile(np.float32([0.5, -0.5, 0.25, 3.0]), K // 4 + 1)[:K]
+    d = synth.random_case(77 + K, 4, K, 40)
+    g, t, Wp, sc = check_pack(d["W"])
+    for n_out in (1, 30, 1000, K - 1):
+        check_a48(X, n_out, t, g, Wp, sc)
