@@ -52,8 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "decode100b_1bit", "ffn",
-                                       "copy"],
+    ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "decode100b_1bit", "a48",
+                                       "ffn", "copy"],
                     help="run one workload's kernels eagerly --steps times and exit "
                          "(for profilers); prints a short JSON line")
     ap.add_argument("--subln", action="store_true",
@@ -128,6 +128,24 @@ def only_workload(args):
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             for i in range(n):
                 B.bitlinear_forward_1bit(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y)
+    elif args.only == "a48":
+        c = synth.DECODE_100B
+        K, N = c["K"], c["N"]
+        p = synth.decode_100b()
+        Wp, sc = B.bitlinear_pack(torch.from_numpy(p["W"]).to(dev))
+        del p["W"]
+        ncp = max(2, int(np.ceil(600e6 / (Wp.numel() * 4))))
+        cps = [Wp.clone() for _ in range(ncp)]
+        n_out = int(round(0.01 * K))
+        for M in (1, 8):
+            Xm = torch.from_numpy(p["X"][:M]).to(dev)
+            q = B.bitlinear_quant_act_a48(Xm, n_out)
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            wsa = torch.empty(B.lib().bitlinear_a48_workspace_bytes(M, N) // 4, dtype=torch.int32,
+                              device=dev)
+            for i in range(n):
+                B.bitlinear_quant_act_a48(Xm, n_out, out=q)
+                B.bitlinear_forward_a48(q, K, cps[i % ncp], sc, N, out=Y, ws=wsa)
     elif args.only == "ffn":
         c = synth.FFN_2B
         D, F = c["D"], c["F"]

@@ -207,6 +207,10 @@ size_t bitlinear_a48_workspace_bytes(int64_t M, int64_t N);
  *  bitlinear_forward.
  *  ws       >= bitlinear_a48_workspace_bytes(M, N) bytes, 16-byte aligned;
  *           after the call it holds acc4 [M][N] then acc8 [M][N] int32.
+ *  Layout hint: when the two parts are stacked -- Xq8 == Xq4 + M * Kp,
+ *  x8_scale == x4_scale + M and x8_rowsum == x4_rowsum + M -- and M <= 8,
+ *  one product over the 2M code rows reads the weights once instead of
+ *  twice.  Results are identical either way.
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP.
  */
 int bitlinear_forward_a48(const int8_t *Xq4, const float *x4_scale, const int32_t *x4_rowsum,

@@ -201,12 +201,12 @@ def bitlinear_quant_act_a48(X, n_out, out=None):
     dev = X.device
     kp = padded_k(K)
     if out is None:
-        out = {"q4": torch.empty((M, kp), dtype=torch.int8, device=dev),
-               "g4": torch.empty(M, dtype=torch.float32, device=dev),
-               "rs4": torch.empty(M, dtype=torch.int32, device=dev),
-               "q8": torch.empty((M, kp), dtype=torch.int8, device=dev),
-               "g8": torch.empty(M, dtype=torch.float32, device=dev),
-               "rs8": torch.empty(M, dtype=torch.int32, device=dev)}
+        # stacked (int8 part right after the int4 part): the layout the
+        # product runs in one pass for up to 8 tokens
+        q = torch.empty((2, M, kp), dtype=torch.int8, device=dev)
+        g = torch.empty((2, M), dtype=torch.float32, device=dev)
+        r = torch.empty((2, M), dtype=torch.int32, device=dev)
+        out = {"q4": q[0], "g4": g[0], "rs4": r[0], "q8": q[1], "g8": g[1], "rs8": r[1]}
     o = out
     st = lib().bitlinear_quant_act_a48(
         _dev(X, "X"), dt, M, K, int(n_out), _dev(o["q4"], "Xq4"), _dev(o["g4"], "x4_scale"),

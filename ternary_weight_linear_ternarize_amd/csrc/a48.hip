@@ -18,8 +18,9 @@
 //  * gemv_a48_kernel (one token): the GEMV of gemv.hip with both code
 //    vectors in LDS and the masked weight fields shared by the two dot
 //    products (Dot16x2);
-//  * more tokens: the product kernels run once per code matrix with their
-//    int32 accumulators kept, then a48_combine_kernel forms y.
+//  * more tokens: the product kernels run with their int32 accumulators kept
+//    (once over both code matrices when they are stacked and 2M <= 16, else
+//    once per code matrix), then a48_combine_kernel forms y.
 #include "bl_device.h"
 #include "bl_launch.h"
 
@@ -424,10 +425,17 @@ hipError_t launch_forward_a48(const int8_t* x4, const float* g4, const int32_t* 
     if (C <= 128) return gemv_a48_go<2, 4>(a, s);
     return gemv_a48_go<4, 2>(a, s);
   }
-  // two products with their accumulators kept, then the combination
-  hipError_t e = launch_mfma(x4, g4, rs4, M, K, Wp, ws, N, Y, acc, M > 64, s);
-  if (e != hipSuccess) return e;
-  e = launch_mfma(x8, g8, rs8, M, K, Wp, ws, N, Y, acc + M * N, M > 64, s);
+  hipError_t e;
+  if (2 * M <= 16 && x8 == x4 + M * Kp && g8 == g4 + M && rs8 == rs4 + M) {
+    // codes, scales and row sums stacked (the int8 rows right after the int4
+    // rows): one product over 2M rows streams the weights once, and its
+    // accumulators land as acc4 then acc8
+    e = launch_mfma(x4, g4, rs4, 2 * M, K, Wp, ws, N, nullptr, acc, false, s);
+  } else {
+    // two products with their accumulators kept
+    e = launch_mfma(x4, g4, rs4, M, K, Wp, ws, N, Y, acc, M > 64, s);
+    if (e == hipSuccess) e = launch_mfma(x8, g8, rs8, M, K, Wp, ws, N, Y, acc + M * N, M > 64, s);
+  }
   if (e != hipSuccess) return e;
   const int64_t total = M * N;
   hipLaunchKernelGGL(a48_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,

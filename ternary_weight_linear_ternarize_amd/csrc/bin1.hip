@@ -271,7 +271,7 @@ hipError_t launch_forward_1bit(const int8_t* Xq, const float* xs, const int32_t*
     if (C <= 192) return gemv1_go<3, 2>(a, s);
     return gemv1_go<4, 2>(a, s);
   }
-  if (stream_1bit_ok(M, K)) return launch_stream_1bit(Xq, xs, rs, M, K, Wb, ws, N, Y, acc_out, s);
+  if (stream_1bit_ok(M, K, N)) return launch_stream_1bit(Xq, xs, rs, M, K, Wb, ws, N, Y, acc_out, s);
   for (int64_t m0 = 0; m0 < M; m0 += 64) {
     const int64_t ms = M - m0 < 64 ? M - m0 : 64;
     const int8_t* x = Xq + m0 * Kp;

@@ -28,8 +28,9 @@ hipError_t launch_forward_a48(const int8_t* x4, const float* g4, const int32_t* 
                               float* Y, int32_t* acc, hipStream_t s);
 
 // The streaming skinny MFMA kernel on 1-bit binary weights (M <= 16 while
-// the activations fit its LDS: stream_1bit_ok).
-bool stream_1bit_ok(int64_t M, int64_t K);
+// the activations fit its LDS, or on layers of at least 1600 tiles of 16
+// rows with the activations staged in phases: stream_1bit_ok).
+bool stream_1bit_ok(int64_t M, int64_t K, int64_t N);
 hipError_t launch_stream_1bit(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
                               int64_t M, int64_t K, const uint32_t* Wb, const float* w_scale,
                               int64_t N, float* Y, int32_t* acc_out, hipStream_t s);

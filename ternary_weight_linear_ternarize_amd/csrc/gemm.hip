@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
           const int64_t n = n0 + 16 * (wn * TN + tn) + li;
           if (n < N) {
             const int a = acc[0][tm][tn][r] - rsm;
-            Y[m * N + n] = dequant_fast(a, sc);
+            if (Y) Y[m * N + n] = dequant_fast(a, sc);
             if (acc_out) acc_out[m * N + n] = a;
           }
         }
@@ -263,13 +263,14 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
 // and the partial accumulators of waves 1 .. KS-1 are added to wave 0's
 // through LDS before the epilogue (more waves in flight for layers with few
 // rows, e.g. the FFN's down projection).
-template <int NB, int LPR, int WPB, int D, int EPI, int KS, int BITS = 2>
+template <int NB, int LPR, int WPB, int D, int EPI, int KS, int BITS = 2, bool PH = false>
 __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int M, int64_t Kp, int64_t Kw,
     const uint32_t* __restrict__ W0, const float* __restrict__ s0,
     const uint32_t* __restrict__ W1, const float* __restrict__ s1, int64_t N,
-    float* __restrict__ Y, int32_t* __restrict__ acc_out, float* __restrict__ gh_parts) {
+    float* __restrict__ Y, int32_t* __restrict__ acc_out, float* __restrict__ gh_parts,
+    int sph) {
   static_assert(BITS == 2 || BITS == 1, "2-bit codes or the 1-bit binary layout");
   constexpr int STEP = LPR * 64 * (2 / BITS);    // weights per row per step (16 B per lane)
   constexpr int RPI = 64 / LPR;                  // rows per load instruction
@@ -282,7 +283,10 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = wave / KS, kpart = wave % KS;
   const int g = lane >> 4, li = lane & 15;
-  const int64_t pitch = Kp + 16;                 // staged activation row
+  // PH: the activations are staged sph steps at a time (M x Kp does not fit
+  // next to the weight patches); otherwise all of K at once
+  const int64_t kph = PH && (int64_t)sph * STEP < Kp ? (int64_t)sph * STEP : Kp;
+  const int64_t pitch = kph + 16;                // staged activation row
   int8_t* lds_x = lds;
   const int64_t xbytes = staged_rows_bytes(M, pitch);
   int8_t* lds_w = lds + xbytes + (int64_t)wave * NB * 16 * BP;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   for (int d = 0; d < D; ++d)
     if (d < nsteps) load_step(d, st[d]);
   // activations -> LDS, every load in flight at once
-  stage_rows_lds<64 * WPB>(Xq, Kp, M, 0, (int)Kp, (int)pitch, lds_x);
+  stage_rows_lds<64 * WPB>(Xq, Kp, M, 0, (int)kph, (int)pitch, lds_x);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -340,16 +344,31 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   for (int mat = 0; mat < NB; ++mat) acc[mat][0] = acc[mat][1] = v4i{0, 0, 0, 0};
   const bool arow = li < M;
   const int8_t* xrow = lds_x + (arow ? li : 0) * pitch + 64 * g;
+  int64_t xbase = 0;   // K position of the first staged column
+  int next_ph = sph;   // step at which the next phase is staged
 
   for (int sbase = 0; sbase < nsteps; sbase += D) {
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     const int sidx = sbase + d;
     if (sidx >= nsteps) break;
+    const int sabs = s_begin + sidx;
+    if (PH && sabs == next_ph) {
+      // next phase of the activations (KS == 1 only: every wave of the block
+      // is at the same step); the weight patches are wave-private
+      __syncthreads();
+      xbase = (int64_t)sabs * STEP;
+      stage_rows_lds<64 * WPB>(Xq, Kp, M, xbase, (int)(Kp - xbase < kph ? Kp - xbase : kph),
+                               (int)pitch, lds_x);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      next_ph += sph;
+    }
     stage_step(st[d]);
     wave_sync();
     if (sidx + D < nsteps) load_step(sidx + D, st[d]);
-    const int64_t k0 = (int64_t)(s_begin + sidx) * STEP;
+    const int64_t k0 = (int64_t)sabs * STEP;
+    const int64_t kx = PH ? k0 - xbase : k0;  // k0 within the staged phase
 #pragma unroll
     for (int b = 0; b < STEP / 256; ++b) {
       if (k0 + 256 * b < Kw) {
@@ -370,7 +389,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
         for (int s = 0; s < 4; ++s) {
           const int64_t ka = k0 + 256 * b + 64 * g + 16 * s;  // this lane's activation bytes
           v4i a = v4i{0, 0, 0, 0};
-          if (arow && ka < Kp) a = *reinterpret_cast<const v4i*>(xrow + k0 + 256 * b + 16 * s);
+          if (arow && ka < Kp) a = *reinterpret_cast<const v4i*>(xrow + kx + 256 * b + 16 * s);
 #pragma unroll
           for (int mat = 0; mat < NB; ++mat) {
             v4i bv;
@@ -418,7 +437,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
       const int m = 4 * g + r;
       if (owner && m < M && n < N) {
         const int a = acc[0][0][r] - rowsum[m];
-        Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
+        if (Y) Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
     }
@@ -473,27 +492,33 @@ static void allow_lds(Kern k) {
 constexpr int kStreamLpr = 16;
 constexpr int kStreamBp = kStreamLpr * 16 + 16;  // staged bytes per weight row and step
 
-static int64_t stream_lds_bytes(int64_t M, int64_t Kp, int nb, int wpb, int ks) {
-  return staged_rows_bytes(M, Kp + 16) + (int64_t)wpb * nb * 16 * kStreamBp +
+// kx: activation columns staged at a time (Kp, or a phase of whole steps)
+static int64_t stream_lds_bytes(int64_t M, int64_t kx, int nb, int wpb, int ks) {
+  return staged_rows_bytes(M, kx + 16) + (int64_t)wpb * nb * 16 * kStreamBp +
          (int64_t)(wpb / ks) * (ks - 1) * nb * 1024;
 }
 
-template <int NB, int WPB, int KS, int EPI, int BITS>
+// Large layers (>= 1600 tiles of 16 rows) at up to 16 tokens whose M x Kp
+// activations do not fit next to 8 waves' weight patches: staged in phases.
+static bool stream_phased_ok(int64_t M, int64_t N) { return M <= 16 && (N + 15) / 16 >= 200 * 8; }
+
+template <int NB, int WPB, int KS, int EPI, int BITS, bool PH = false>
 static hipError_t stream_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                             int64_t Kp, int64_t Kw, const uint32_t* W0, const float* s0,
                             const uint32_t* W1, const float* s1, int64_t N, float* Y,
-                            int32_t* acc_out, float* gh_parts, int* nparts, hipStream_t s) {
+                            int32_t* acc_out, float* gh_parts, int* nparts, hipStream_t s,
+                            int sph, int64_t kx) {
   constexpr int TPB = WPB / KS;
-  const size_t lds = (size_t)stream_lds_bytes(M, Kp, NB, WPB, KS);
+  const size_t lds = (size_t)stream_lds_bytes(M, kx, NB, WPB, KS);
   const unsigned blocks = (unsigned)((N + 16 * TPB - 1) / (16 * TPB));
   if (nparts) *nparts = (int)blocks;
   constexpr int D = 1;  // steps of weights in flight (2 and 4 measured slower: VGPR pressure)
   static bool once =
-      (allow_lds(mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS>), true);
+      (allow_lds(mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS, PH>), true);
   (void)once;
-  hipLaunchKernelGGL((mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS>), dim3(blocks),
+  hipLaunchKernelGGL((mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS, PH>), dim3(blocks),
                      dim3(64 * WPB), lds, s, Xq, xs, rs, (int)M, Kp, Kw, W0, s0, W1, s1, N, Y,
-                     acc_out, gh_parts);
+                     acc_out, gh_parts, sph);
   return hipGetLastError();
 }
 
@@ -508,11 +533,26 @@ static hipError_t stream_launch(const int8_t* Xq, const float* xs, const int32_t
   const int64_t Kw = BITS == 2 ? Kp : (Kp + 127) / 128 * 128;  // weights per row
   auto fits = [&](int wpb, int ks) { return stream_lds_bytes(M, Kp, NB, wpb, ks) <= kStreamLds; };
   const int64_t tiles = (N + 15) / 16;
-  const int64_t nsteps = (Kw + 64 * kStreamLpr * (2 / BITS) - 1) / (64 * kStreamLpr * (2 / BITS));
+  constexpr int64_t STEP = 64 * kStreamLpr * (2 / BITS);
+  const int64_t nsteps = (Kw + STEP - 1) / STEP;
+  int sph = (int)nsteps;
+  int64_t kx = Kp;
 #define BL_STREAM_GO(WPB, KS)                                                                 \
   return stream_go<NB, WPB, KS, EPI, BITS>(Xq, xs, rs, M, Kp, Kw, W0, s0, W1, s1, N, Y,       \
-                                           acc_out, gh_parts, nparts, s)
+                                           acc_out, gh_parts, nparts, s, sph, kx)
   if (tiles >= 200 * 8 && fits(8, 1)) BL_STREAM_GO(8, 1);
+  if (stream_phased_ok(M, N)) {
+    // fewest phases that fit next to 8 waves' patches
+    for (int64_t P = 2; P <= nsteps; ++P) {
+      sph = (int)((nsteps + P - 1) / P);
+      kx = sph * STEP < Kp ? sph * STEP : Kp;
+      if (stream_lds_bytes(M, kx, NB, 8, 1) <= kStreamLds)
+        return stream_go<NB, 8, 1, EPI, BITS, true>(Xq, xs, rs, M, Kp, Kw, W0, s0, W1, s1, N, Y,
+                                                    acc_out, gh_parts, nparts, s, sph, kx);
+    }
+    sph = (int)nsteps;
+    kx = Kp;
+  }
   if (tiles >= 200 * 4 && fits(4, 1)) BL_STREAM_GO(4, 1);
   if (tiles >= 200 * 2 && fits(2, 1)) BL_STREAM_GO(2, 1);
   if (tiles >= 200 || nsteps < 2) BL_STREAM_GO(1, 1);
@@ -542,8 +582,12 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
   if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
-  if (direct_ok(M, K, N, 1)) return launch_direct(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
-  if (stream_ok(M, Kp))
+  // large layers: the streaming kernel with 8-wave blocks (activations staged
+  // in phases when they do not fit), 18.5 us against the direct kernel's
+  // 39.5 us on the 100B-class layer at 16 tokens
+  if (!stream_phased_ok(M, N) && direct_ok(M, K, N, 1))
+    return launch_direct(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
+  if (stream_ok(M, Kp) || stream_phased_ok(M, N))
     return stream_launch<1, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
                                       nullptr, nullptr, s);
   if (M <= 16)
@@ -558,7 +602,9 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                                            acc_out, nullptr, nullptr, s);
 }
 
-bool stream_1bit_ok(int64_t M, int64_t K) { return stream_ok(M, (K + 63) / 64 * 64); }
+bool stream_1bit_ok(int64_t M, int64_t K, int64_t N) {
+  return stream_ok(M, (K + 63) / 64 * 64) || stream_phased_ok(M, N);
+}
 
 hipError_t launch_stream_1bit(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                               int64_t K, const uint32_t* Wb, const float* ws, int64_t N, float* Y,

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
       const int m = 4 * g + r;
       if (owner && m < M && n < N) {
         const int a = acc[0][0][r] - rowsum[m];
-        Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
+        if (Y) Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
     }

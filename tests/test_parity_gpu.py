@@ -375,6 +375,28 @@ def test_decode_100b_binary_1bit_full():
         check_forward1(q, gx, t, g, Xq, xs, xr, Wb, sc)
 
 
+def test_skinny_phased_activations_large_layer():
+    # 16 tokens, K = 8192, N = 25600 (1600 tiles of 16 rows): the activation
+    # block does not fit next to 8 waves' weight patches and is staged in
+    # phases; 2-bit ternary and 1-bit binary layouts, sampled columns
+    M, K, N = 16, 8192, 25600
+    d = synth.random_case(1717, M, K, N)
+    g, t, Wp, sc = check_pack(d["W"])
+    g1, t1, Wb, sc1 = check_pack1(d["W"])
+    del d["W"]
+    q, gx, rs, Xq, xs, xr = check_quant(d["X"])
+    cols = np.unique(np.concatenate([np.arange(0, N, 101), [N - 1]]))
+    runs = ((t, g, lambda **kw: B.bitlinear_forward(Xq, xs, xr, K, Wp, sc, N, **kw)),
+            (t1, g1, lambda **kw: B.bitlinear_forward_1bit(Xq, xs, xr, K, Wb, sc1, N, **kw)))
+    for tt, gw, fwd in runs:
+        Y, A = fwd(with_acc=True)
+        acc = oracle.int_linear(q, tt[cols])
+        np.testing.assert_array_equal(host(A)[:, cols], acc)
+        assert_rel(host(Y)[:, cols], oracle.dequant(acc, gx, gw))
+        Y2 = fwd()
+        np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
 # ----------------------------------------------------------------------------
 # BitNet a4.8 split activations (int8 outliers + int4 rest)
 
@@ -439,3 +461,24 @@ def test_a48_quant_degenerate_rows(K):
     g, t, Wp, sc = check_pack(d["W"])
     for n_out in (1, 30, 1000, K - 1):
         check_a48(X, n_out, t, g, Wp, sc)
+
+
+def test_a48_stacked_and_separate_layouts_agree():
+    # the stacked quantiser output (one product over 2M rows for M <= 8) and
+    # the same codes in separate buffers (two products) give identical bits
+    d = synth.random_case(909, 8, 3000, 500)
+    X = synth.with_outliers(d["X"], synth.outlier_columns(909, 3000))
+    g, t, Wp, sc = check_pack(d["W"])
+    K, N = 3000, 500
+    for M in (2, 8):
+        q = B.bitlinear_quant_act_a48(to_dev(X[:M]), 30)
+        assert q["q8"].data_ptr() == q["q4"].data_ptr() + q["q4"].numel()
+        sep = {k: v.clone() for k, v in q.items()}
+        Y1, ws1 = B.bitlinear_forward_a48(q, K, Wp, sc, N)
+        Y2, ws2 = B.bitlinear_forward_a48(sep, K, Wp, sc, N)
+        np.testing.assert_array_equal(host(ws1)[:2 * M * N], host(ws2)[:2 * M * N])
+        np.testing.assert_array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+        ref = oracle.bitlinear_a48(X[:M], t, g, 30)
+        acc = host(ws1)[:2 * M * N].reshape(2, M, N)
+        np.testing.assert_array_equal(acc[0], ref["acc4"])
+        np.testing.assert_array_equal(acc[1], ref["acc8"])
