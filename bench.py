@@ -30,13 +30,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# HBM bytes per launch of the dominant kernel from rocprofv3 counters
-# (profiles/gemv_fused_decode_2b.md: FETCH_SIZE x 1.9998 + WRITE_SIZE, the
-# factors a plain 256 MiB copy reads back).  Valid for this kernel build
-# only: set to None whenever the kernel changes until the counters are
-# taken again.
-UP_GEMV_KERNEL = "gemv_kernel<1,4,0,1,512>"
-UP_GEMV_TRAFFIC_BYTES = 4632322
+# The decode step's two kernels and their HBM bytes per launch from rocprofv3
+# counters (profiles/gemv_fused_decode_2b.md: FETCH_SIZE x 1.9998 +
+# WRITE_SIZE, the factors a plain 256 MiB copy reads back).  Valid for these
+# kernel builds only: set a figure to None whenever its kernel changes until
+# the counters are taken again.
+DECODE_GEMVS = {
+    "up": ("gemv_kernel<1,4,0,1,512>", 4632318, "2560->6912"),
+    "down": ("gemv_kernel<2,2,0,1,512>", 4785851, "6912->2560"),
+}
 
 METRIC = ("BitLinear W1.58A8: decode GEMV weight GB/s (% HBM peak); "
           "prefill int8 TOPS (% MFMA)")
@@ -294,8 +296,9 @@ def main():
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / ne
 
-    # ---------------- dominant kernel: the fused up GEMV, HIP events around
-    # graph replays of back-to-back launches over the rotating copies
+    # ---------------- dominant kernel: the slower of the step's two fused
+    # GEMVs, HIP events around graph replays of back-to-back launches over
+    # the rotating copies
     up_ms = graph_time_per_launch(
         lambda i: B.bitlinear_forward_fused(x, ups[i % copies], sup, N, out=y1, ws=ws1),
         copies, 10, torch)
@@ -304,14 +307,20 @@ def main():
         copies, 10, torch)
     alg_up = pbytes + K * 4 + 4 + N * 4      # packed W + fp32 x + w_scale + fp32 y
     alg_dn = pbytes + N * 4 + 4 + K * 4
-    achieved = alg_up / (up_ms * 1e-3) / 1e9
+    legs = {"up": (up_ms, alg_up), "down": (dn_ms, alg_dn)}
+    dom = max(legs, key=lambda leg: legs[leg][0])
+    dom_ms, dom_alg = legs[dom]
+    kname, traffic, shape = DECODE_GEMVS[dom]
+    achieved = dom_alg / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": UP_GEMV_TRAFFIC_BYTES,
-                "kernel": UP_GEMV_KERNEL + " (fused quant + GEMV, 2560->6912, M=1)",
-                "avg_us": round(up_ms * 1e3, 3), "algorithmic_bytes": alg_up}
+                "traffic": traffic,
+                "kernel": f"{kname} (fused quant + GEMV, {shape}, M=1; the slower of the "
+                          "step's two kernels)",
+                "avg_us": round(dom_ms * 1e3, 3), "algorithmic_bytes": dom_alg}
     kernels = {
-        "gemv_fused_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3), "GBps": round(achieved, 1)},
+        "gemv_fused_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3),
+                                    "GBps": round(alg_up / (up_ms * 1e-3) / 1e9, 1)},
         "gemv_fused_down_6912x2560": {"avg_us": round(dn_ms * 1e3, 3),
                                       "GBps": round(alg_dn / (dn_ms * 1e-3) / 1e9, 1)},
         "decode_step_eager_us": round(eager_ms * 1e3, 3),
