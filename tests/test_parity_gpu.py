@@ -189,6 +189,29 @@ def test_prefill_2b_sampled_rows():
     np.testing.assert_array_equal(host(Y2).view(np.uint32), hY.view(np.uint32))
 
 
+def test_page_shape_example_512_to_400_on_10x1000_tokens():
+    # [P2] "BitLinear層の基本実装": BitLinear(512, 400) applied to a (10, 1000, 512)
+    # input gives (10, 1000, 400); here the 10 000 tokens run through the
+    # tiled GEMM (78 full token tiles + a 16-row tail, a 144-column tail)
+    d = synth.random_case(5120, 10 * 1000, 512, 400)
+    g, t, Wp, sc = check_pack(d["W"])
+    X3 = to_dev(d["X"]).view(10, 1000, 512)
+    Xq, xs, xr = B.bitlinear_quant_act(X3.reshape(-1, 512))
+    Y, A = B.bitlinear_forward(Xq, xs, xr, 512, Wp, sc, 400, with_acc=True)
+    Y3 = Y.view(10, 1000, 400)
+    assert tuple(Y3.shape) == (10, 1000, 400)
+    q, gx, rs = oracle.act_quant(d["X"])
+    np.testing.assert_array_equal(host(Xq)[:, :512], q)
+    rows = np.unique(np.concatenate([np.arange(0, 10000, 37), [9983, 9999]]))
+    acc = oracle.int_linear(q[rows], t)
+    np.testing.assert_array_equal(host(A)[rows], acc)
+    assert_rel(host(Y)[rows], oracle.dequant(acc, gx[rows], g))
+    cols = np.arange(0, 400, 13)
+    np.testing.assert_array_equal(host(A)[:, cols], q.astype(np.int64) @ t[cols].astype(np.int64).T)
+    Y2 = B.bitlinear_forward(Xq, xs, xr, 512, Wp, sc, 400)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
 @pytest.mark.parametrize("mode", ["ternary", "binary"])
 def test_decode_100b_full(mode):
     d = synth.decode_100b()
