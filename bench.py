@@ -218,8 +218,8 @@ def graph_time_per_launch(fn, n, reps, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: only one GPU is supported in this build (asked for {args.gpus}); "
-              "the multi-GPU split is a design note, not a measured path.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for {args.gpus}); splitting the "
+              "layers across GPUs is a design note, not a measured path.", file=sys.stderr)
         sys.exit(2)
     if args.only:
         print(json.dumps(only_workload(args)), flush=True)

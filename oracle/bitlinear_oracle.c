@@ -148,7 +148,7 @@ void orc_binarize(const float *w, int64_t n, int8_t *t) {
 /* ------------------------------------------------------------------------ */
 /* Packed 2-bit layout.  [P1] "アーキテクチャ概要" and [P3] §2.3: 2 bits per
  * weight, code 00 = -1, 01 = 0, 10 = +1, sixteen weights per 32-bit word.
- * Layout of this build (the pages leave the bit order open):
+ * Layout used here (the pages leave the bit order open):
  *   row n holds Kp = K rounded up to 64 weights as Kp/16 words;
  *   word j covers weights 16j .. 16j+15;
  *   weight 16j + 4s + b sits in byte b of the word, at bits 2s and 2s+1;
@@ -195,7 +195,7 @@ int64_t orc_unpack(const uint32_t *packed, int64_t N, int64_t K, int8_t *t) {
 /* ------------------------------------------------------------------------ */
 /* Packed 1-bit layout for the binary variant ([P1] "1-Bit重みとSign関数":
  * W_b = Sign(W) has two values, so one bit per weight suffices; [P2] counts
- * the 1-bit memory saving).  Layout of this build:
+ * the 1-bit memory saving).  Layout used here:
  *   row n holds Kb = K rounded up to 128 weights as Kb/32 words;
  *   word j covers weights 32j .. 32j+31;
  *   weight 32j + 4s + b (s = 0..7, b = 0..3) is bit 8b + s of the word;
@@ -275,7 +275,7 @@ void orc_act_quant(const float *x, int64_t M, int64_t K, int8_t *q, float *gamma
 }
 
 /* [P1] "BitNet a4.8": activations in 4 bits, with the top fraction of the
- * values (the outliers) split off and kept in 8 bits.  Reading of this build
+ * values (the outliers) split off and kept in 8 bits.  Reading taken here
  * (the page gives no formulas): per token row, the n_out entries of largest
  * |x| (ties to the lower index) are outliers; they are quantised like
  * activation_quant with Q = 127 and their own scale g8 = their max |x|; all

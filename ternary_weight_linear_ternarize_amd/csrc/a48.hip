@@ -2,7 +2,7 @@
 // a4.8"): the top fraction of each token's activations is split off and kept
 // in 8 bits, the rest is quantised to 4 bits.
 //
-// Reading of this build: per token row the n_out entries of largest |x|
+// Reading taken here: per token row the n_out entries of largest |x|
 // (ties to the lower index) are the outliers, quantised like the int8
 // activation quantiser (Q = 127) with their own scale g8 = max |x| over them;
 // every other entry is quantised with Q = 7 (symmetric 4-bit range) and
