@@ -69,6 +69,20 @@ __device__ __forceinline__ int a48_code(float x, float q, float d) {
   return (int)r;
 }
 
+// The same code with the division by d done by Markstein's correction from
+// y = RN(1/d) (as quant_code_fast): RN(q0 + r y) with q0 = RN(a y) and the
+// exact residual r = a - q0 d is the correctly rounded a / d while d and 1/d
+// are normal (fast rows: 1e-5 <= d < 2^100); a / d only matters near k + 1/2,
+// where a is normal.
+__device__ __forceinline__ int a48_code_fast(float x, float q, float d, float y) {
+  const float a = __fmul_rn(x, q);
+  const float q0 = __fmul_rn(a, y);
+  const float r = __builtin_fmaf(-q0, d, a);
+  float v = __builtin_rintf(__builtin_fmaf(r, y, q0));
+  v = fminf(fmaxf(v, -q), q);
+  return (int)v;
+}
+
 // Thread t owns indices t E .. t E + E - 1 (index order = thread order).
 //
 // The n_out-th largest key T (key = the bits of |x|, bit 31 clear) is found
@@ -101,8 +115,29 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
   const char* row = reinterpret_cast<const char*>(X) + m * K * (BF16 ? 2 : 4);
 
   float v[E];
+  const bool vec = k0 + E <= K && (reinterpret_cast<uintptr_t>(row) & (BF16 ? 7 : 15)) == 0;
+  if (vec) {
+    // E / 4 loads of 4 consecutive values (the row start is aligned)
 #pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = (k0 + e < K) ? load_act<BF16>(row, k0 + e) : 0.0f;
+    for (int j = 0; j < E / 4; ++j) {
+      if constexpr (BF16) {
+        const uint2 u = reinterpret_cast<const uint2*>(row)[k0 / 4 + j];
+        v[4 * j + 0] = __uint_as_float(u.x << 16);
+        v[4 * j + 1] = __uint_as_float(u.x & 0xffff0000u);
+        v[4 * j + 2] = __uint_as_float(u.y << 16);
+        v[4 * j + 3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        const float4 f = reinterpret_cast<const float4*>(row)[k0 / 4 + j];
+        v[4 * j + 0] = f.x;
+        v[4 * j + 1] = f.y;
+        v[4 * j + 2] = f.z;
+        v[4 * j + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = (k0 + e < K) ? load_act<BF16>(row, k0 + e) : 0.0f;
+  }
   auto key = [&](int e) { return __float_as_uint(v[e]) & 0x7fffffffu; };
 
   const int nsel = n_out < K ? n_out : (int)K;
@@ -210,6 +245,8 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
     a4 = fmaxf(a4, shf[1][w]);
   }
   const float d8 = __fadd_rn(a8, kEps), d4 = __fadd_rn(a4, kEps);
+  const float y8 = __fdiv_rn(1.0f, d8), y4 = __fdiv_rn(1.0f, d4);
+  const bool fast = d8 < 0x1p100f && d4 < 0x1p100f;
 
   int s4 = 0, s8 = 0;
   uint32_t w4[E / 4], w8[E / 4];
@@ -219,8 +256,13 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
   for (int e = 0; e < E; ++e) {
     int c4 = 0, c8 = 0;
     if (k0 + e < K) {
-      if (out[e]) c8 = a48_code(v[e], kQ, d8);
-      else c4 = a48_code(v[e], 7.0f, d4);
+      if (fast) {
+        if (out[e]) c8 = a48_code_fast(v[e], kQ, d8, y8);
+        else c4 = a48_code_fast(v[e], 7.0f, d4, y4);
+      } else {
+        if (out[e]) c8 = a48_code(v[e], kQ, d8);
+        else c4 = a48_code(v[e], 7.0f, d4);
+      }
     }
     s4 += c4;
     s8 += c8;
