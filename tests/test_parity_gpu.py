@@ -189,6 +189,21 @@ def test_prefill_2b_sampled_rows():
     np.testing.assert_array_equal(host(Y2).view(np.uint32), hY.view(np.uint32))
 
 
+def test_skinny_phased_activations_ragged_k():
+    # the phased staging with a K that ends inside a step (Kp = 7040: the
+    # second phase stages 2944 columns and its last step reads past Kp)
+    M, K, N = 16, 7000, 25600
+    d = synth.random_case(1718, M, K, N)
+    g, t, Wp, sc = check_pack(d["W"])
+    del d["W"]
+    q, gx, rs, Xq, xs, xr = check_quant(d["X"])
+    cols = np.unique(np.concatenate([np.arange(5, N, 97), [N - 1]]))
+    Y, A = B.bitlinear_forward(Xq, xs, xr, K, Wp, sc, N, with_acc=True)
+    acc = oracle.int_linear(q, t[cols])
+    np.testing.assert_array_equal(host(A)[:, cols], acc)
+    assert_rel(host(Y)[:, cols], oracle.dequant(acc, gx, g))
+
+
 def test_page_shape_example_512_to_400_on_10x1000_tokens():
     # [P2] "BitLinear層の基本実装": BitLinear(512, 400) applied to a (10, 1000, 512)
     # input gives (10, 1000, 400); here the 10 000 tokens run through the
