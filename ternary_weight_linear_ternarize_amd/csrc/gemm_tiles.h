@@ -116,11 +116,16 @@ __global__ __launch_bounds__(256, MINB) void tiled_gemm_kernel(
     a_pl[j] = (lane & 15) ^ (row & 15);
     a_off[j] = (uint32_t)(row * Kp + 16 * a_pl[j]);
   }
+  // 32-bit range tests (K is far below 2^31): piece j of this lane is in
+  // range while kc < a_lim[j]
+  int a_lim[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) a_lim[j] = (int)Kp - 16 * a_pl[j];
   auto issue_a = [&](int c, int buf) {
-    const int64_t kc = (int64_t)c * KCH;
+    const int kc = c * KCH;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const uint32_t off = (kc + 16 * a_pl[j] < Kp) ? a_off[j] + (uint32_t)kc : kOOB;
+      const uint32_t off = kc < a_lim[j] ? a_off[j] + (uint32_t)kc : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds + buf * ABYTES + (wave * NLD + j) * 1024, 16,
                                                off, 0, 0, 0);
     }
@@ -129,14 +134,14 @@ __global__ __launch_bounds__(256, MINB) void tiled_gemm_kernel(
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn)
     b_off[tn] = (uint32_t)(((32 * (wn * TN + tn) + li) * wpr + 8 * g) * 4);
+  const int b_lim = (int)wpr - 8 * g;  // words w0 + 4q + (0..3) in range while w0 + 4q < b_lim
   auto issue_b = [&](int c, u32x4 (&dst)[TN][2]) {
-    const int64_t w0 = (int64_t)c * (KCH / 16);
+    const int w0 = c * (KCH / 16);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const uint32_t off =
-            (w0 + 8 * g + 4 * q < wpr) ? b_off[tn] + (uint32_t)((w0 + 4 * q) * 4) : kOOB;
+        const uint32_t off = w0 + 4 * q < b_lim ? b_off[tn] + (uint32_t)((w0 + 4 * q) * 4) : kOOB;
         dst[tn][q] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
       }
   };
