@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "decode100b_1bit", "a48",
-                                       "ffn", "copy"],
+                                       "ffn", "pack", "copy"],
                     help="run one workload's kernels eagerly --steps times and exit "
                          "(for profilers); prints a short JSON line")
     ap.add_argument("--subln", action="store_true",
@@ -148,6 +148,14 @@ def only_workload(args):
             for i in range(n):
                 B.bitlinear_quant_act_a48(Xm, n_out, out=q)
                 B.bitlinear_forward_a48(q, K, cps[i % ncp], sc, N, out=Y, ws=wsa)
+    elif args.only == "pack":
+        # weight preparation of the 100B-class matrix (absmean scale + packing), each layout
+        p = synth.decode_100b()
+        Wd = torch.from_numpy(p["W"]).to(dev)
+        del p
+        for mode in (B.BL_TERNARY, B.BL_BINARY, B.BL_BINARY_1BIT):
+            for i in range(n):
+                B.bitlinear_pack(Wd, mode)
     elif args.only == "ffn":
         c = synth.FFN_2B
         D, F = c["D"], c["F"]

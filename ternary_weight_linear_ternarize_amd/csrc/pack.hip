@@ -22,27 +22,76 @@ __global__ void zero_bins_kernel(uint64_t* bins) {
   if (i < kBins) bins[i] = 0ull;
 }
 
-// Grid-stride over all n weights; per-wave LDS bins, then one global atomic
-// add per non-empty bin per block.  Integer adds: the result does not depend
-// on the order.
+// Grid-stride over 4-weight units (a float4 load when W is 16-byte aligned,
+// two units in flight per lane).  Each lane sums exactly in a 128-bit integer
+// A (four 32-bit limbs) at a fixed scale: with window base lo, a weight of bin
+// b in [lo, lo + 64) adds m * 2^(b - lo), so A * 2^(lo - 150) is the lane's
+// sum.  lo is set from the lane's first non-zero weight (40 bins below it);
+// weights outside the window go straight into the block's LDS bins.  At the
+// end limb j of A is added to bin lo + 32 j (same value, bin form), and the
+// block adds its non-empty bins to the global ones.  Bounds: each add is below
+// 2^87 and a lane adds at most 2^13 weights (n <= 2^32), so A < 2^128; lo is
+// kept in [1, 159] so that lo + 96 is a bin.  Integer adds throughout: the
+// result does not depend on the order.
+__device__ __forceinline__ void absmean_add(float x, int& lo, uint32_t (&a)[4],
+                                            unsigned long long* lbins) {
+  int b;
+  uint32_t m;
+  bin_of(x, b, m);
+  if (lo == 0 && m != 0u) lo = min(max(b - 40, 1), 159);
+  const int sh = b - lo;
+  if ((unsigned)sh < 64u || m == 0u) {
+    const uint64_t p = (uint64_t)m << (sh & 31);
+    const uint32_t p0 = (uint32_t)p, p1 = (uint32_t)(p >> 32);
+    const bool hi = sh >= 32;
+    uint64_t t = (uint64_t)a[0] + (hi ? 0u : p0);
+    a[0] = (uint32_t)t;
+    t = (uint64_t)a[1] + (hi ? p0 : p1) + (t >> 32);
+    a[1] = (uint32_t)t;
+    t = (uint64_t)a[2] + (hi ? p1 : 0u) + (t >> 32);
+    a[2] = (uint32_t)t;
+    a[3] += (uint32_t)(t >> 32);
+  } else {
+    atomicAdd(&lbins[b], (unsigned long long)m);
+  }
+}
+
 __global__ __launch_bounds__(256) void absmean_bins_kernel(const float* __restrict__ W,
-                                                           int64_t n, uint64_t* bins) {
-  __shared__ unsigned long long lbins[4][kBins];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < 4 * kBins; i += 256) (&lbins[0][0])[i] = 0ull;
+                                                           int64_t n, bool vec, uint64_t* bins) {
+  __shared__ unsigned long long lbins[kBins];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins; i += 256) lbins[i] = 0ull;
   __syncthreads();
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + tid; i < n; i += stride) {
-    int b;
-    uint32_t m;
-    bin_of(W[i], b, m);
-    if (m) atomicAdd(&lbins[wave][b], (unsigned long long)m);
+  const int64_t units = (n + 3) / 4;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int lo = 0;
+  uint32_t a[4] = {0u, 0u, 0u, 0u};
+  for (int64_t u0 = (int64_t)blockIdx.x * 256 + tid; u0 < units; u0 += 2 * stride) {
+    float x[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t u = u0 + h * stride;
+      if (vec && 4 * u + 3 < n) {
+        const float4 f = reinterpret_cast<const float4*>(W)[u];
+        x[h][0] = f.x; x[h][1] = f.y; x[h][2] = f.z; x[h][3] = f.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[h][i] = 4 * u + i < n ? W[4 * u + i] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) absmean_add(x[h][i], lo, a, lbins);
+  }
+  if (lo != 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (a[j]) atomicAdd(&lbins[lo + 32 * j], (unsigned long long)a[j]);
   }
   __syncthreads();
-  for (int b = tid; b < kBins; b += 256) {
-    unsigned long long v = lbins[0][b] + lbins[1][b] + lbins[2][b] + lbins[3][b];
-    if (v) atomicAdd(reinterpret_cast<unsigned long long*>(&bins[b]), v);
-  }
+  for (int b = tid; b < kBins; b += 256)
+    if (lbins[b]) atomicAdd(reinterpret_cast<unsigned long long*>(&bins[b]), lbins[b]);
 }
 
 __global__ __launch_bounds__(64) void absmean_finalize_kernel(const uint64_t* __restrict__ bins,
@@ -56,82 +105,94 @@ __global__ __launch_bounds__(64) void absmean_finalize_kernel(const uint64_t* __
   if (threadIdx.x == 0) w_scale[0] = (float)(s / (double)n);
 }
 
-// One thread per packed word.  Row n, word j covers weights 16j..16j+15;
-// weight 16j + 4s + b goes to byte b, bits 2s..2s+1, as code t + 1; weights
-// past K are code 01.
-template <bool BINARY>
-__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int64_t N,
-                                                   int64_t K, int64_t words_per_row,
+// Packing, one lane per four consecutive weights of a row (a float4 load when
+// rows are 16-byte aligned, so a wave reads 1 KiB of contiguous weights), the
+// lanes that share an output word combining their parts with shuffles.
+//   MODE 0/1 (ternary / binary, 2-bit codes): word j of a row covers weights
+//     16j..16j+15; weight 16j + 4s + b goes to byte b, bits 2s..2s+1, as code
+//     t + 1; weights past K are code 01.  Four lanes per word.
+//   MODE 2 (binary, 1-bit layout): word j covers weights 32j..32j+31; weight
+//     32j + 4s + b is bit 8b + s, 1 for w >= 0 (+1) and 0 for w < 0 (-1);
+//     weights past K (rows padded to 128) are bit 0.  Eight lanes per word.
+// Block b covers row b / bpr, 4-weight units [1024 (b % bpr), +1024) of it;
+// upr (units per padded row) is a multiple of the lanes per word.
+template <int MODE>
+__global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, int64_t K,
+                                                   int64_t upr, int bpr, bool vec,
                                                    const float* __restrict__ w_scale,
                                                    uint32_t* __restrict__ Wp) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= N * words_per_row) return;
-  const int64_t n = idx / words_per_row, j = idx - n * words_per_row;
-  const float d = __fadd_rn(w_scale[0], kEps);
-  const float* row = W + n * K;
-  uint32_t word = 0u;
+  constexpr int L = MODE == 2 ? 8 : 4;  // lanes per word
+  constexpr int U = 4;                  // units per lane
+  const int blk = (int)blockIdx.x;
+  const int n = blk / bpr, seg = blk - n * bpr;
+  const float* row = W + (int64_t)n * K;
+  uint32_t* out = Wp + (int64_t)n * (upr / L);
+  const float d = MODE == 0 ? __fadd_rn(w_scale[0], kEps) : 1.0f;
+  float w[U][4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t k = 16 * j + r;
-    uint32_t code = 1u;
-    if (k < K) {
-      const float w = row[k];
-      if constexpr (BINARY) {
-        code = (w >= 0.0f) ? 2u : 0u;
+  for (int i = 0; i < U; ++i) {
+    const int64_t k0 = 4 * ((int64_t)(seg * U + i) * 256 + threadIdx.x);
+    if (vec && k0 + 3 < K) {
+      const float4 f = *reinterpret_cast<const float4*>(row + k0);
+      w[i][0] = f.x; w[i][1] = f.y; w[i][2] = f.z; w[i][3] = f.w;
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w[i][b] = k0 + b < K ? row[k0 + b] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < U; ++i) {
+    const int64_t v = (int64_t)(seg * U + i) * 256 + threadIdx.x;  // unit within the row
+    const int s = (int)(v % L);
+    uint32_t part = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bool in = 4 * v + b < K;
+      if constexpr (MODE == 2) {
+        part |= (in && w[i][b] >= 0.0f ? 1u : 0u) << (8 * b + s);
       } else {
-        float q = __builtin_rintf(__fdiv_rn(w, d));
-        q = fminf(fmaxf(q, -1.0f), 1.0f);
-        code = (uint32_t)((int)q + 1);
+        uint32_t code = 1u;
+        if (in) {
+          if constexpr (MODE == 1) {
+            code = w[i][b] >= 0.0f ? 2u : 0u;
+          } else {
+            float q = __builtin_rintf(__fdiv_rn(w[i][b], d));
+            q = fminf(fmaxf(q, -1.0f), 1.0f);
+            code = (uint32_t)((int)q + 1);
+          }
+        }
+        part |= code << (8 * b + 2 * s);
       }
     }
-    const int s = r >> 2, b = r & 3;
-    word |= code << (8 * b + 2 * s);
+    part |= __shfl_xor(part, 1);
+    part |= __shfl_xor(part, 2);
+    if constexpr (L == 8) part |= __shfl_xor(part, 4);
+    if (s == 0 && v < upr) out[v / L] = part;
   }
-  Wp[idx] = word;
-}
-
-// 1-bit layout of binary weights, one thread per word: row n, word j covers
-// weights 32j..32j+31; weight 32j + 4s + b is bit 8b + s, 1 for w >= 0 (+1)
-// and 0 for w < 0 (-1); weights past K (rows padded to 128) are bit 0.
-__global__ __launch_bounds__(256) void pack1_kernel(const float* __restrict__ W, int64_t N,
-                                                    int64_t K, int64_t words_per_row,
-                                                    uint32_t* __restrict__ Wp) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= N * words_per_row) return;
-  const int64_t n = idx / words_per_row, j = idx - n * words_per_row;
-  const float* row = W + n * K;
-  uint32_t word = 0u;
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    const int64_t k = 32 * j + r;
-    const uint32_t bit = (k < K && row[k] >= 0.0f) ? 1u : 0u;
-    word |= bit << (8 * (r & 3) + (r >> 2));
-  }
-  Wp[idx] = word;
 }
 
 hipError_t launch_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp,
                        float* w_scale, uint64_t* bins, hipStream_t s) {
   const int64_t n = N * K;
   const int64_t kp = (K + 63) / 64 * 64;
-  const int64_t wpr = kp / 16;
   hipLaunchKernelGGL(zero_bins_kernel, dim3(1), dim3(kBins), 0, s, bins);
-  int64_t blocks = (n + 255) / 256;
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+  const bool vec = aligned16 && K % 4 == 0;
+  int64_t blocks = (n + 1023) / 1024;  // one 4-weight unit per thread at least
   if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(absmean_bins_kernel, dim3((unsigned)blocks), dim3(256), 0, s, W, n, bins);
+  hipLaunchKernelGGL(absmean_bins_kernel, dim3((unsigned)blocks), dim3(256), 0, s, W, n,
+                     aligned16, bins);
   hipLaunchKernelGGL(absmean_finalize_kernel, dim3(1), dim3(64), 0, s, bins, n, w_scale);
-  if (mode == 2) {
-    const int64_t wpr1 = (K + 127) / 128 * 4;
-    const unsigned b1 = (unsigned)((N * wpr1 + 255) / 256);
-    hipLaunchKernelGGL(pack1_kernel, dim3(b1), dim3(256), 0, s, W, N, K, wpr1, Wp);
-    return hipGetLastError();
-  }
-  const int64_t total = N * wpr;
-  const unsigned pblocks = (unsigned)((total + 255) / 256);
-  if (mode == 1)
-    hipLaunchKernelGGL(pack_kernel<true>, dim3(pblocks), dim3(256), 0, s, W, N, K, wpr, w_scale, Wp);
+  const int64_t kpad = mode == 2 ? (K + 127) / 128 * 128 : kp;
+  const int64_t upr = kpad / 4;
+  const int bpr = (int)((upr + 1023) / 1024);
+  const unsigned pb = (unsigned)(N * bpr);
+  if (mode == 2)
+    hipLaunchKernelGGL(pack_kernel<2>, dim3(pb), dim3(256), 0, s, W, K, upr, bpr, vec, w_scale, Wp);
+  else if (mode == 1)
+    hipLaunchKernelGGL(pack_kernel<1>, dim3(pb), dim3(256), 0, s, W, K, upr, bpr, vec, w_scale, Wp);
   else
-    hipLaunchKernelGGL(pack_kernel<false>, dim3(pblocks), dim3(256), 0, s, W, N, K, wpr, w_scale, Wp);
+    hipLaunchKernelGGL(pack_kernel<0>, dim3(pb), dim3(256), 0, s, W, K, upr, bpr, vec, w_scale, Wp);
   return hipGetLastError();
 }
 

@@ -145,6 +145,30 @@ def test_binary_mode_and_degenerate_weights():
     assert g == np.float32(1.0 / 128)
 
 
+def test_weight_scale_wide_dynamic_range():
+    """Weights spread over the whole binary32 range (subnormals to 2^120, zeros
+    of both signs, rows of one magnitude) so the absmean sum takes every path:
+    the in-window integer accumulators, the direct bins and their merge."""
+    rng = np.random.default_rng(41)
+    for (N, K) in ((96, 1000), (37, 301)):
+        W = rng.standard_normal((N, K)).astype(np.float32)
+        W *= np.ldexp(np.float32(1), rng.integers(-140, 121, size=(N, K))).astype(np.float32)
+        W[0, :] = np.float32(1e-45)           # smallest subnormal
+        W[1, :] = -0.0
+        W[2, ::3] = 0.0
+        W[3, :] = np.float32(3.0e38)
+        W[4, :] = rng.standard_normal(K).astype(np.float32) * np.float32(2.0 ** -30)
+        for mode in ("ternary", "binary"):
+            check_pack(W, mode)
+        # the same values from a base address that is not 16-byte aligned
+        flat = to_dev(np.concatenate([np.zeros(1, np.float32), W.ravel()]))
+        Wd = flat[1:].view(N, K)
+        Wp, sc = B.bitlinear_pack(Wd)
+        g, t, pk = oracle.quantize_weights(W, "ternary")
+        np.testing.assert_array_equal(host(Wp).view(np.uint32), pk)
+        assert host(sc)[0].view(np.uint32) == np.float32(g).view(np.uint32)
+
+
 def test_quant_edge_rows_and_bf16():
     X = synth.normal(22, 1, (6, 700))
     X[1] = 0.0
