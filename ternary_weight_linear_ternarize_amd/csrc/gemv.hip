@@ -404,7 +404,8 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, const int32_t* rs, int
 }
 
 // The fused kernels redo the row's quantisation in every block; past ~7K
-// inputs that redundant work costs more than a separate quantisation launch.
+// inputs that redundant work costs more than a separate quantisation launch
+// (8192 -> 28672: 15.5 us fused, 14.5 us for the quantiser and the int8 GEMV).
 bool gemv_fused_ok(int64_t K) { return (K + 63) / 64 * 64 <= kFusedMaxKp; }
 
 hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t* Wp,
