@@ -26,7 +26,12 @@
  *    Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *    and runs asynchronously; results are valid after the caller
  *    synchronises that stream.  Calls on different streams that share no
- *    output buffer may run concurrently; the library holds no global state.
+ *    output buffer or workspace may run concurrently; the library keeps no
+ *    state between calls (beyond one-time kernel attributes).
+ *  - Only kernel launches are enqueued (no memset, copy or event), so a
+ *    sequence of calls can be captured in a HIP graph and replayed; the
+ *    pointers passed at capture time, workspaces included, stay baked into
+ *    the graph.
  *  - Validation is host-only and happens before anything is enqueued; on
  *    any error nothing is launched and no memory is touched.  Device
  *    pointers are never dereferenced on the host.
