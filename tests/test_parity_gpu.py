@@ -304,7 +304,7 @@ def test_ffn_2b_fp32(M):
     _ffn_case(M, False, "ones")
 
 
-@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("M", [1, 8, 64])
 def test_ffn_2b_bf16_random_norm(M):
     _ffn_case(M, True, "random")
 
