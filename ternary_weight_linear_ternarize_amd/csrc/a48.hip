@@ -20,7 +20,9 @@
 //    products (Dot16x2);
 //  * more tokens: the product kernels run with their int32 accumulators kept
 //    (once over both code matrices when they are stacked and 2M <= 16, else
-//    once per code matrix), then a48_combine_kernel forms y.
+//    once per code matrix), then a48_combine_kernel forms y; where the
+//    stacked product runs on the streaming kernel, its epilogue forms y and
+//    there is no combine launch.
 #include "bl_device.h"
 #include "bl_launch.h"
 
@@ -299,13 +301,6 @@ __global__ __launch_bounds__(1024) void a48_quant_kernel(const void* __restrict_
   }
 }
 
-// y = (acc4 (g_w g4)) / 7 + (acc8 (g_w g8)) / 127, one rounding per operation.
-__device__ __forceinline__ float a48_dequant(int acc4, float s4, int acc8, float s8) {
-  const float y4 = __fdiv_rn(__fmul_rn((float)acc4, s4), 7.0f);
-  const float y8 = __fdiv_rn(__fmul_rn((float)acc8, s8), kQ);
-  return __fadd_rn(y4, y8);
-}
-
 struct A48Args {
   const int8_t* x4;
   const int8_t* x8;
@@ -468,7 +463,10 @@ hipError_t launch_forward_a48(const int8_t* x4, const float* g4, const int32_t* 
     return gemv_a48_go<4, 2>(a, s);
   }
   hipError_t e;
-  if (2 * M <= 16 && x8 == x4 + M * Kp && g8 == g4 + M && rs8 == rs4 + M) {
+  const bool stacked = x8 == x4 + M * Kp && g8 == g4 + M && rs8 == rs4 + M;
+  if (stacked && stream_a48_ok(2 * M, K, N))
+    return launch_stream_a48(x4, g4, rs4, 2 * M, K, Wp, ws, N, Y, acc, s);
+  if (2 * M <= 16 && stacked) {
     // codes, scales and row sums stacked (the int8 rows right after the int4
     // rows): one product over 2M rows streams the weights once, and its
     // accumulators land as acc4 then acc8

@@ -580,6 +580,15 @@ __device__ float block_meansq(const float (&xv)[NWT][4], int64_t D, SumsqScratch
 // int8 in natural order.  Three of the four fields are used in place (scaled
 // by 4 and 16) and rescaled exactly afterwards; all values stay < 2^7 per
 // byte so the signed 8-bit dot product is exact.
+// BitNet a4.8 output from the two accumulators of a token:
+// y = (acc4 (g_w g4)) / 7 + (acc8 (g_w g8)) / 127, one rounding per operation
+// (s4 = g_w g4 and s8 = g_w g8 already rounded).
+__device__ __forceinline__ float a48_dequant(int acc4, float s4, int acc8, float s8) {
+  const float y4 = __fdiv_rn(__fmul_rn((float)acc4, s4), 7.0f);
+  const float y8 = __fdiv_rn(__fmul_rn((float)acc8, s8), kQ);
+  return __fadd_rn(y4, y8);
+}
+
 struct Dot16 {
   int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
   __device__ __forceinline__ void add(uint32_t w, int x0, int x1, int x2, int x3) {

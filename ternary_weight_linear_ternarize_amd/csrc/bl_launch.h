@@ -92,6 +92,14 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* x_scale, const int3
 // Up to 16 tokens with the weights loaded straight into MFMA operands
 // (skinny.hip); direct_ok says whether the shape is covered (LDS, registers).
 bool direct_ok(int64_t M, int64_t K, int64_t N, int nb);
+// a4.8 codes stacked as 2 Mh rows (int4 rows, then the int8 rows of the same
+// tokens, scales and row sums stacked alike): where the product runs on the
+// streaming kernel, one launch writes both accumulators (acc4 then acc8 rows)
+// and y of the Mh tokens (gemm.hip).
+bool stream_a48_ok(int64_t M2, int64_t K, int64_t N);
+hipError_t launch_stream_a48(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M2,
+                             int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                             int32_t* acc, hipStream_t s);
 hipError_t launch_direct(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,
                          int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s);

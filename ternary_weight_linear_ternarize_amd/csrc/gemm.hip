@@ -30,7 +30,9 @@
 
 namespace bl {
 
-enum { MF_STORE = 0, MF_GATEUP = 1 };
+// MF_A48: a4.8 codes stacked as 2 Mh rows (the int4 rows of Mh tokens, then
+// their int8 rows); the streaming kernel forms y of the Mh tokens itself.
+enum { MF_STORE = 0, MF_GATEUP = 1, MF_A48 = 2 };
 
 hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
@@ -441,6 +443,31 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
     }
+  } else if constexpr (EPI == MF_A48) {
+    // rows m and m + Mh of the tile are token m's int4 and int8 parts; the
+    // wave trades its accumulators through its own weight patch (free after
+    // the last step) so the lane of row m sees both
+    const float sw = s0[0];
+    const int Mh = M / 2;
+    int av[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      av[r] = m < M ? acc[0][0][r] - rowsum[m] : 0;
+      if (owner && m < M && n < N && acc_out) acc_out[(int64_t)m * N + n] = av[r];
+    }
+    int* ex = reinterpret_cast<int*>(lds_w);
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ex[(4 * g + r) * 16 + li] = av[r];
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      if (owner && m < Mh && n < N)
+        Y[(int64_t)m * N + n] = a48_dequant(av[r], __fmul_rn(sw, x_scale[m]),
+                                            ex[(m + Mh) * 16 + li], __fmul_rn(sw, x_scale[m + Mh]));
+    }
   } else {
     const float sg = s0[0], su = s1[0];
 #pragma unroll
@@ -592,9 +619,9 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
   if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
-  // large layers: the streaming kernel with 8-wave blocks (activations staged
-  // in phases when they do not fit), 18.5 us against the direct kernel's
-  // 39.5 us on the 100B-class layer at 16 tokens
+  // large layers: the streaming kernel with 7- or 8-wave blocks (activations
+  // staged in phases when they do not fit), 18.5 us against the direct
+  // kernel's 39.5 us on the 100B-class layer at 16 tokens
   if (!stream_phased_ok(M, N) && direct_ok(M, K, N, 1))
     return launch_direct(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   if (stream_ok(M, Kp) || stream_phased_ok(M, N))
@@ -610,6 +637,23 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                                              acc_out, nullptr, nullptr, s);
   return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                            acc_out, nullptr, nullptr, s);
+}
+
+// The stacked a4.8 product (M2 = 2 Mh code rows) where launch_mfma runs the
+// streaming kernel: that kernel then writes y too (no combine launch).
+bool stream_a48_ok(int64_t M2, int64_t K, int64_t N) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  if (M2 > 16 || M2 % 2 != 0) return false;
+  if (!stream_phased_ok(M2, N) && direct_ok(M2, K, N, 1)) return false;
+  return stream_ok(M2, Kp) || stream_phased_ok(M2, N);
+}
+
+hipError_t launch_stream_a48(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M2,
+                             int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                             int32_t* acc, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  return stream_launch<1, MF_A48>(Xq, xs, rs, M2, Kp, Wp, ws, nullptr, nullptr, N, Y, acc,
+                                  nullptr, nullptr, s);
 }
 
 bool stream_1bit_ok(int64_t M, int64_t K, int64_t N) {
