@@ -441,6 +441,93 @@ def test_rmsnorm_close_to_exact_and_special_rows():
     np.testing.assert_allclose(y, yt, rtol=3e-6, atol=1e-6)
 
 
+def _sum_of_squares(target):
+    """Integers a_i < 2^24 with sum a_i^2 == target (greedy, a handful of terms)."""
+    out = []
+    while target > 0:
+        a = math.isqrt(target)
+        out.append(a)
+        target -= a * a
+    assert all(a < 2 ** 24 for a in out)
+    return out
+
+
+def _midpoint_rows(D, count, seed):
+    """Rows x = a * 2^e whose exact mean square sum(x^2) / D lies exactly on a
+    binary32 rounding midpoint (odd 25-bit significand) or one unit of the sum
+    away from it, so that every rounding step of the mean square is decided
+    by the last bit."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(count):
+        odd = (1 << 24) + 2 * int(rng.integers(0, 1 << 23)) + 1  # a midpoint's significand
+        target = D * odd + (0, 1, -1)[i % 3]
+        a = _sum_of_squares(target)
+        row = np.zeros(D, np.float32)
+        pos = rng.choice(D, size=len(a), replace=False)
+        e = int(rng.integers(-40, -10))
+        sign = np.where(rng.random(len(a)) < 0.5, -1.0, 1.0)
+        row[pos] = (sign * np.ldexp(np.array(a, np.float64), e)).astype(np.float32)
+        assert (row[pos].astype(np.float64) == sign * np.ldexp(np.array(a, np.float64), e)).all()
+        rows.append(row)
+    return np.stack(rows)
+
+
+def _rmsnorm_f32(x, g, eps, mean_square=None, scale=None):
+    """RMSNorm re-expressed with numpy binary32 scalars: ms = binary32(fsum(x^2)
+    / D) (the exact sum rounded once to binary64, a binary64 division, one
+    rounding to binary32), r = 1 / sqrt(ms + eps) in binary32, y = (x * r) * g.
+    mean_square / scale replace those two steps (to plant mistakes)."""
+    D = x.shape[1]
+    out = np.empty_like(x)
+    for m in range(x.shape[0]):
+        xr = x[m].astype(np.float64)
+        if mean_square is None:
+            ms = np.float32(math.fsum(xr * xr) / D)
+        else:
+            ms = mean_square(x[m])
+        r = np.float32(1) / np.sqrt(ms + np.float32(eps))
+        out[m] = (x[m] * r) * g if scale is None else scale(x[m], r, g)
+    return out
+
+
+def test_rmsnorm_bits_match_an_independent_float32_expression():
+    # random rows with a random weight, plus rows whose mean square sits on or
+    # next to a binary32 rounding midpoint (2560 and 6912 wide: the block's D
+    # and F, where the division by D is not exact)
+    eps = np.float32(np.finfo(np.float32).eps)
+    cases = []
+    x = synth.normal(21, 1, (1000, 2560))
+    g = (np.float32(1) + synth.normal(21, 2, (2560,), 0.1)).astype(np.float32)
+    cases.append((x, g))
+    for D, seed in ((2560, 22), (6912, 23), (64, 24)):
+        xm = _midpoint_rows(D, 60, seed)
+        gm = (np.float32(1) + synth.normal(seed, 3, (D,), 0.1)).astype(np.float32)
+        cases.append((xm, gm))
+    for xc, gc in cases:
+        y = oracle.rmsnorm(xc, gc, float(eps))
+        ref = _rmsnorm_f32(xc, gc, eps)
+        np.testing.assert_array_equal(y.view(np.uint32), ref.view(np.uint32))
+        y1 = oracle.rmsnorm(xc, None, float(eps))
+        ref1 = _rmsnorm_f32(xc, np.ones(xc.shape[1], np.float32), eps)
+        np.testing.assert_array_equal(y1.view(np.uint32), ref1.view(np.uint32))
+    # the comparison has teeth: plausible slips each change some bits
+    xr, gr = cases[0]
+    xm = cases[1][0]  # mean squares on or next to midpoints, D = 2560
+    slips = {
+        "x*(r*g)": (xr, gr, dict(scale=lambda v, r, gg: v * (r * gg))),
+        "(float)s/D": (xm, None, dict(mean_square=lambda v: np.float32(
+            np.float32(math.fsum(v.astype(np.float64) ** 2)) / np.float32(v.size)))),
+        "float32 running sum": (xr[:50], gr, dict(mean_square=lambda v: np.float32(
+            np.add.reduce(v * v, dtype=np.float32) / np.float32(v.size)))),
+    }
+    for name, (xs, gs, kw) in slips.items():
+        gw = gs if gs is not None else np.ones(xs.shape[1], np.float32)
+        bad = _rmsnorm_f32(xs, gw, eps, **kw)
+        good = oracle.rmsnorm(xs, gw, float(eps))
+        assert not np.array_equal(bad.view(np.uint32), good.view(np.uint32)), name
+
+
 # ----------------------------------------------------------------------------
 # a7/a8: FFN
 
@@ -488,6 +575,19 @@ def test_ffn_zero_cases():
 
 # ----------------------------------------------------------------------------
 # SubLN variant of the FFN: RMSNorm of h (over F) before the down quantiser
+
+def test_relu2_mul_matches_torch_float32():
+    g = synth.normal(25, 1, (300_000,))
+    u = synth.normal(25, 2, (300_000,))
+    g[:7] = [0.0, -0.0, 1e-30, -1e-30, 3e19, -3e19, 1.5]
+    h = oracle.relu2_mul(g, u)
+    gt, ut = torch.from_numpy(g), torch.from_numpy(u)
+    ref = (torch.relu(gt).square() * ut).numpy()
+    np.testing.assert_array_equal(h.view(np.uint32), ref.view(np.uint32))
+    # the order matters: relu(g) * (relu(g) * u) differs somewhere
+    alt = (torch.relu(gt) * (torch.relu(gt) * ut)).numpy()
+    assert not np.array_equal(h.view(np.uint32), alt.view(np.uint32))
+
 
 def _constant_h_ffn(sign, su):
     """Gate and up rows all +1 (up rows all `sign`) against non-negative
@@ -629,6 +729,28 @@ def test_a48_dequant_closed_form():
     y = oracle.dequant_a48(acc4, np.array([1.0], np.float32), acc8, np.array([2.0], np.float32),
                            np.float32(1.0))
     np.testing.assert_array_equal(y, [[3.0, -2.0, -4.0]])
+
+
+def test_a48_dequant_matches_torch_float32():
+    # the listing's rescale per part, (acc * (w_scale * x_scale)) / Q with
+    # Q = 7 and 127, added in binary32; accumulators over the full int4 / int8
+    # ranges of a 28672 x 8192 layer
+    rng = np.random.default_rng(26)
+    M, N = 8, 40000
+    acc4 = rng.integers(-7 * 8192, 7 * 8192, size=(M, N)).astype(np.int32)
+    acc8 = rng.integers(-127 * 82, 127 * 82, size=(M, N)).astype(np.int32)
+    g4 = (rng.random(M) * 3 + 0.01).astype(np.float32)
+    g8 = (rng.random(M) * 60 + 1).astype(np.float32)
+    gw = np.float32(0.01597)
+    y = oracle.dequant_a48(acc4, g4, acc8, g8, gw)
+    w = torch.tensor(gw)
+    a4, a8 = torch.from_numpy(acc4).float(), torch.from_numpy(acc8).float()
+    s4, s8 = w * torch.from_numpy(g4)[:, None], w * torch.from_numpy(g8)[:, None]
+    ref = ((a4 * s4) / 7 + (a8 * s8) / 127).numpy()
+    np.testing.assert_array_equal(y.view(np.uint32), ref.view(np.uint32))
+    # a different association of the int4 term changes some bits
+    alt = ((a4 * w * torch.from_numpy(g4)[:, None]) / 7 + (a8 * s8) / 127).numpy()
+    assert not np.array_equal(y.view(np.uint32), alt.view(np.uint32))
 
 
 # ----------------------------------------------------------------------------
