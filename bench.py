@@ -7,12 +7,14 @@ BitLinear and the down BitLinear, each one fused launch (per-token absmax
 quantisation, ternary x int8 GEMV, dequant).  Weights are packed once before
 timing (the pages describe packing as a one-time conversion).  The timed
 steps rotate over enough distinct copies of the packed weights (> 512 MB)
-that they stream from HBM, not from the 256 MB last-level cache, and are
-replayed from a HIP graph (launch-bound work; the replay is checked against
-the eager result first).
+that they stream from HBM, not from the 256 MB last-level cache; the cache
+is flushed before the warm-up.  --warmup W untimed steps, then exactly
+--steps K timed steps, each set launched as one HIP graph (the replay is
+checked against the eager result first).
 
 value = packed-weight bytes of both projections per step / wall time per
-step (GB/s), every kernel and the gaps between them included.
+step (GB/s) between synchronisations around the K steps: every kernel, the
+gaps between them and the graph launch included.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-extra]
@@ -30,15 +32,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-# The decode step's two kernels and their HBM bytes per launch from rocprofv3
-# counters (profiles/gemv_fused_decode_2b.md: FETCH_SIZE x 1.9998 +
-# WRITE_SIZE, the factors a plain 256 MiB copy reads back).  Valid for these
-# kernel builds only: set a figure to None whenever its kernel changes until
-# the counters are taken again.
+# The decode step's two kernels (template instances the fused forward
+# launches for these shapes).  Their HBM traffic per launch comes from the
+# rocprofv3 counter summary committed under profiles/, and is reported only
+# while the kernel sources are the ones those counters were taken on.
 DECODE_GEMVS = {
-    "up": ("gemv_kernel<1,4,0,1,512>", 4632318, "2560->6912"),
-    "down": ("gemv_kernel<2,2,0,1,512>", 4785851, "6912->2560"),
+    "up": ("gemv_kernel<1,4,0,1,512>", "2560->6912"),
+    "down": ("gemv_kernel<2,2,0,1,512>", "6912->2560"),
 }
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_fused_decode_2b.md")
+CSRC = os.path.join(ROOT, "ternary_weight_linear_ternarize_amd", "csrc")
 
 METRIC = ("BitLinear W1.58A8: decode GEMV weight GB/s (% HBM peak); "
           "prefill int8 TOPS (% MFMA)")
@@ -55,7 +58,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=["decode", "prefill", "decode100b", "decode100b_1bit", "a48",
-                                       "ffn", "pack", "copy"],
+                                       "ffn", "pack", "copy", "floors"],
                     help="run one workload's kernels eagerly --steps times and exit "
                          "(for profilers); prints a short JSON line")
     ap.add_argument("--subln", action="store_true",
@@ -78,6 +81,20 @@ def only_workload(args):
             b.copy_(a)
         torch.cuda.synchronize()
         return {"only": "copy", "bytes_per_launch": a.numel() * 4, "launches": n}
+    if args.only == "floors":
+        # one-shot reads of the 2B-class (4,423,680 B) and 100B-class (58,720,256 B)
+        # packed matrices, rotating over copies, and an empty kernel
+        sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+        for nbytes in (4423680, 58720256):
+            ncp = max(2, int(np.ceil(600e6 / nbytes)))
+            bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(ncp)]
+            for i in range(n):
+                B.probe_read(bufs[i % ncp], 4, sink)
+            del bufs
+        for i in range(n):
+            B.probe_empty(dev)
+        torch.cuda.synchronize()
+        return {"only": "floors", "launches_per_shape": n}
     if args.only == "decode":
         d = synth.decode_2b()
         K, N = synth.DECODE_2B["K"], synth.DECODE_2B["N"]
@@ -178,6 +195,55 @@ def only_workload(args):
     return {"only": args.only, "launches_per_shape": n}
 
 
+def flush_last_level_cache(torch, dev):
+    """Writes 512 MiB (twice the 256 MB last-level cache) so that nothing the
+    timed steps read is still cached."""
+    buf = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    buf.fill_(1.0)
+    torch.cuda.synchronize()
+    del buf
+
+
+def sources_hash():
+    """sha256 (first 12 hex digits) of the HIP sources and headers."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:12]
+
+
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if
+    it was taken on the current sources; (None, reason) otherwise."""
+    import re
+    cur = sources_hash()
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None, "no counter profile"
+    pat = re.compile(r"^traffic: (\S+) (\d+) B/launch \(sources ([0-9a-f]{12})\)")
+    seen = False
+    for line in open(TRAFFIC_PROFILE):
+        m = pat.match(line.strip())
+        if m and m.group(1) == kernel:
+            seen = True
+            if m.group(3) == cur:
+                return int(m.group(2)), f"{os.path.relpath(TRAFFIC_PROFILE, ROOT)} (sources {cur})"
+    why = "counters taken on other sources" if seen else "kernel not in the counter profile"
+    return None, f"{why}; current sources {cur}"
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def event_time_per_launch(fn, n, torch):
     """Average duration of fn()'s kernel(s), from an event pair around each
     launch on the current stream (the one the binding launches on)."""
@@ -192,13 +258,15 @@ def event_time_per_launch(fn, n, torch):
     return float(np.mean(ms)), float(np.median(ms))
 
 
-def capture(fn, n, torch):
+def capture(fn, n, torch, skip_warm=False):
     """HIP graph of fn(0..n-1) launched back to back on a capture stream."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn_warm = [fn(i) for i in range(min(n, 2))]  # noqa: F841  (eager warm-up on s)
+    if not skip_warm:
+        with torch.cuda.stream(s):
+            for i in range(min(n, 2)):  # eager warm-up on s
+                fn(i)
     torch.cuda.current_stream().wait_stream(s)
     with torch.cuda.graph(g):
         for i in range(n):
@@ -266,32 +334,42 @@ def main():
         B.bitlinear_forward_fused(x, ups[j], sup, N, out=y1, ws=ws1)
         B.bitlinear_forward_fused(xd, dns[j], sdn, K, out=y2, ws=ws2)
 
-    # eager reference of one step, then the graph (one replay = `copies` steps)
+    # eager reference of one step; the graph replay must reproduce it
     step(0)
     torch.cuda.synchronize()
     ref1, ref2 = y1.clone(), y2.clone()
-    graph = capture(step, copies, torch)
-    for _ in range(3):
+    K_steps, W_steps = args.steps, args.warmup
+    # steps W .. W+K-1 (copy i % copies) are timed; each copy was last read at
+    # least `copies` steps (> 512 MB of weights) earlier, or never since the
+    # cache flush below
+    warm = capture(lambda i: step(i), W_steps, torch, skip_warm=True) if W_steps > 0 else None
+    timed = capture(lambda i: step(W_steps + i), K_steps, torch, skip_warm=True)
+    check = capture(lambda i: step(i), 1, torch, skip_warm=True)
+    for _ in range(2):
         y1.zero_()
         y2.zero_()
-        graph.replay()
+        check.replay()
         torch.cuda.synchronize()
         if not (torch.equal(y1, ref1) and torch.equal(y2, ref2)):
             raise RuntimeError("graph replay differs from the eager step")
-    reps = max(1, args.steps // copies)
-    wreps = max(1, args.warmup // copies)
-    steps = reps * copies
-    for _ in range(wreps):
-        graph.replay()
+    flush_last_level_cache(torch, dev)
+    if warm is not None:
+        warm.replay()
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
+    e0.record(stream)
+    timed.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / steps
+    ms_step = (t1 - t0) * 1e3 / K_steps
+    ev_ms_step = e0.elapsed_time(e1) / K_steps
     step_bytes = 2 * pbytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    del warm, timed, check
 
     # eager (one launch per call from Python), for context
     for i in range(20):
@@ -307,25 +385,30 @@ def main():
     # ---------------- dominant kernel: the slower of the step's two fused
     # GEMVs, HIP events around graph replays of back-to-back launches over
     # the rotating copies
+    nl = max(K_steps, copies)
     up_ms = graph_time_per_launch(
         lambda i: B.bitlinear_forward_fused(x, ups[i % copies], sup, N, out=y1, ws=ws1),
-        copies, 10, torch)
+        nl, 1, torch)
     dn_ms = graph_time_per_launch(
         lambda i: B.bitlinear_forward_fused(xd, dns[i % copies], sdn, K, out=y2, ws=ws2),
-        copies, 10, torch)
+        nl, 1, torch)
     alg_up = pbytes + K * 4 + 4 + N * 4      # packed W + fp32 x + w_scale + fp32 y
     alg_dn = pbytes + N * 4 + 4 + K * 4
     legs = {"up": (up_ms, alg_up), "down": (dn_ms, alg_dn)}
     dom = max(legs, key=lambda leg: legs[leg][0])
     dom_ms, dom_alg = legs[dom]
-    kname, traffic, shape = DECODE_GEMVS[dom]
+    kname, shape = DECODE_GEMVS[dom]
     achieved = dom_alg / (dom_ms * 1e-3) / 1e9
+    traffic, traffic_note = traffic_from_profile(kname)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
                 "kernel": f"{kname} (fused quant + GEMV, {shape}, M=1; the slower of the "
                           "step's two kernels)",
-                "avg_us": round(dom_ms * 1e3, 3), "algorithmic_bytes": dom_alg}
+                "avg_us": round(dom_ms * 1e3, 3), "algorithmic_bytes": dom_alg,
+                "timing": f"HIP events around one replay of a graph of {nl} back-to-back "
+                          "launches on the launch stream (weight copies rotating)",
+                "traffic_source": traffic_note}
     kernels = {
         "gemv_fused_up_2560x6912": {"avg_us": round(up_ms * 1e3, 3),
                                     "GBps": round(alg_up / (up_ms * 1e-3) / 1e9, 1)},
@@ -345,14 +428,17 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": steps, "warmup": wreps * copies, "ms_per_step": round(ms_step, 6),
+        "steps": K_steps, "warmup": W_steps, "ms_per_step": round(ms_step, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "decode 2B-class: M=1, BitLinear 2560->6912 + 6912->2560 from fp32 "
                                "activations, ternary 2-bit packed weights ~N(0,0.02), x ~N(0,1), "
                                "int8 per-token quantisation fused into each GEMV",
                    "M": 1, "K": K, "N": N, "weight_copies": copies,
-                   "step_weight_bytes": step_bytes, "launch": "HIP graph of back-to-back steps",
+                   "step_weight_bytes": step_bytes,
+                   "launch": "one HIP graph of the K timed steps, wall clock between "
+                             "synchronisations (graph launch included)",
+                   "event_ms_per_step": round(ev_ms_step, 6),
                    "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
     }
@@ -506,7 +592,7 @@ def cpu_baseline(d, seconds, step_bytes):
             break
     dt = time.perf_counter() - t0
     return {"value": round(step_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "ms_per_step": round(dt * 1e3 / n, 3),
+            "kind": "oracle", "cpu_model": cpu_model(), "ms_per_step": round(dt * 1e3 / n, 3),
             "sample": f"{n} oracle decode steps (quant + int matmul + dequant, up and down) "
                       f"in {dt:.1f} s; same packed-weight byte count per step as the GPU"}
 

@@ -135,7 +135,8 @@ int bitlinear_pack(const float *W, int64_t N, int64_t K, int mode, uint32_t *Wp,
  *  Xq       [M][Kp] int8, device, 16-byte aligned, written; columns K..Kp-1
  *           are written as 0.
  *  x_scale  [M] float, device, written with g_m = max_k |x[m][k]|.
- *  x_rowsum [M] int32, device, written with sum_k q[m][k]; may be NULL.
+ *  x_rowsum [M] int32, device, written with sum_k q[m][k] (required: the
+ *           product kernels of bitlinear_forward take it as an input).
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EHIP.
  */
 int bitlinear_quant_act(const void *X, int dtype, int64_t M, int64_t K, int8_t *Xq,
@@ -294,7 +295,9 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F);
  *           the 2B-class FFN workload states it).  subln_eps: its epsilon.
  *  Wg, Wu   [F][Dp/16] packed (16-byte aligned), sg, su their scales.
  *  Wd       [D][Fp/16] packed, sd its scale.
- *  Y        [M][D] float32, device, written.
+ *  Y        [M][D] float32, device, 4-byte aligned, written (16-byte
+ *           alignment lets 17..64 tokens take the split-K down projection;
+ *           the result is the same either way).
  *  ws       >= bitnet_ffn_workspace_bytes(M, D, F) bytes, 256-byte aligned.
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP.
  */

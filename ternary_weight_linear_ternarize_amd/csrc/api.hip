@@ -79,11 +79,11 @@ int bitlinear_pack(const float* W, int64_t N, int64_t K, int mode, uint32_t* Wp,
 
 int bitlinear_quant_act(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
                         float* x_scale, int32_t* x_rowsum, void* stream) {
-  if (!X || !Xq || !x_scale) return BL_EINVAL;
+  if (!X || !Xq || !x_scale || !x_rowsum) return BL_EINVAL;
   if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
   if (!m_ok(M) || !dim_ok(K)) return BL_ESHAPE;
   if (!aligned(X, dtype == BL_F32 ? 4 : 2) || !aligned(Xq, 16) || !aligned(x_scale, 4) ||
-      (x_rowsum && !aligned(x_rowsum, 4)))
+      !aligned(x_rowsum, 4))
     return BL_EALIGN;
   return hip_status(bl::launch_act_quant(X, dtype == BL_BF16, M, K, Xq, x_scale, x_rowsum,
                                          nullptr, 0, as_stream(stream)));
@@ -275,11 +275,15 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   hipStream_t s = as_stream(stream);
   const bool bf16 = dtype == BL_BF16;
 
-  const bool split = ffn_splitk(M, D, F);
+  // the split-K reduction stores Y in 16-byte vectors; other callers take the
+  // single-pass kernels (same bits)
+  const bool split = ffn_splitk(M, D, F) && aligned(Y, 16);
   hipError_t e = bl::launch_rmsnorm_quant(H, bf16, M, D, norm_w, norm_eps, xn, qx, gx, rsx, s);
   if (e != hipSuccess) return BL_EHIP;
   int nparts = 0;
-  if (M == 1)
+  // one token: the gate/up GEMV while the row fits its K range, else the
+  // MFMA gate/up kernels (which take any K)
+  if (M == 1 && bl::gemv_gateup_ok(D))
     e = bl::launch_gemv_gateup(qx, gx, rsx, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
   else
     e = bl::launch_mfma_gateup(qx, gx, rsx, M, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);

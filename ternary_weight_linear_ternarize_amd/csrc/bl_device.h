@@ -254,11 +254,15 @@ __device__ double finalize_bins(const uint64_t* bins, unsigned long long* limbs,
 // consecutive weights in natural order, ready for a 4-wide int8 dot product
 // or an MFMA operand.
 
-__device__ __forceinline__ void unpack_word(uint32_t w, int& c0, int& c1, int& c2, int& c3) {
-  c0 = (int)(w & 0x03030303u);
-  c1 = (int)((w >> 2) & 0x03030303u);
-  c2 = (int)((w >> 4) & 0x03030303u);
-  c3 = (int)((w >> 6) & 0x03030303u);
+// The four shifted-code byte vectors of one packed word: element s holds the
+// codes of weights 16j+4s .. 16j+4s+3 (one MFMA operand dword each).
+__device__ __forceinline__ v4i codes_operand(uint32_t w) {
+  v4i r;
+  r[0] = (int)(w & 0x03030303u);
+  r[1] = (int)((w >> 2) & 0x03030303u);
+  r[2] = (int)((w >> 4) & 0x03030303u);
+  r[3] = (int)((w >> 6) & 0x03030303u);
+  return r;
 }
 
 // ---------------------------------------------------------------------------

@@ -79,7 +79,9 @@ hipError_t launch_mfma(const int8_t* Xq, const float* x_scale, const int32_t* ro
                        int32_t* acc_out, bool tiled, hipStream_t s);
 
 // FFN gate/up: h = relu(deq(gate))^2 * deq(up) for both weights at once, plus
-// per-block partial maxima of |h| (gh_parts[p * M + m], p < *nparts).
+// per-block partial maxima of |h| (gh_parts[p * M + m], p < *nparts).  The
+// one-token GEMV form covers padded K up to 16384 (gemv_gateup_ok).
+bool gemv_gateup_ok(int64_t K);
 hipError_t launch_gemv_gateup(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
                               int64_t K, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,

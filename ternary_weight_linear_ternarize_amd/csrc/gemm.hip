@@ -41,15 +41,6 @@ hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, i
 constexpr int kChunk = 256;         // K per chunk
 constexpr int kLdsPitch = 256 + 16; // bytes per staged activation row
 
-__device__ __forceinline__ v4i unpack_operand(uint32_t w) {
-  v4i r;
-  r[0] = (int)(w & 0x03030303u);
-  r[1] = (int)((w >> 2) & 0x03030303u);
-  r[2] = (int)((w >> 4) & 0x03030303u);
-  r[3] = (int)((w >> 6) & 0x03030303u);
-  return r;
-}
-
 __device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
   return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
@@ -170,7 +161,7 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
       for (int mat = 0; mat < NB; ++mat) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-          const v4i b = unpack_operand(pick(b_cur[mat][tn], s));
+          const v4i b = codes_operand(pick(b_cur[mat][tn], s));
 #pragma unroll
           for (int tm = 0; tm < TM; ++tm)
             acc[mat][tm][tn] =
@@ -396,7 +387,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
           for (int mat = 0; mat < NB; ++mat) {
             v4i bv;
             if constexpr (BITS == 2) {
-              bv = unpack_operand(s == 0 ? bw[mat].x : s == 1 ? bw[mat].y : s == 2 ? bw[mat].z : bw[mat].w);
+              bv = codes_operand(s == 0 ? bw[mat].x : s == 1 ? bw[mat].y : s == 2 ? bw[mat].z : bw[mat].w);
             } else {
               const uint32_t wd = s < 2 ? bw[mat].x : bw[mat].y;
               bv = (s & 1) ? bits_operand<1>(wd) : bits_operand<0>(wd);
@@ -632,10 +623,7 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                                              acc_out, nullptr, nullptr, s);
   // 17 <= M <= 64: 32 x 32 block tiles (four 16 x 16 wave tiles) keep more
   // blocks in flight than 64-row tiles for these weight-streaming shapes
-  if (M <= 64)
-    return mfma_launch<1, 1, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
-                                             acc_out, nullptr, nullptr, s);
-  return mfma_launch<4, 4, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+  return mfma_launch<1, 1, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                            acc_out, nullptr, nullptr, s);
 }
 

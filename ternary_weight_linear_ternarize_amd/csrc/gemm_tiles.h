@@ -5,17 +5,6 @@
 
 namespace bl {
 
-// The four shifted-code byte vectors of one packed word (weights 16j + 4s + b
-// of the word sit in byte b of vector s).
-__device__ __forceinline__ v4i unpack_operand32(uint32_t w) {
-  v4i r;
-  r[0] = (int)(w & 0x03030303u);
-  r[1] = (int)((w >> 2) & 0x03030303u);
-  r[2] = (int)((w >> 4) & 0x03030303u);
-  r[3] = (int)((w >> 6) & 0x03030303u);
-  return r;
-}
-
 __device__ __forceinline__ uint32_t pick32(const u32x4& v, int s) {
   return s == 0 ? v[0] : s == 1 ? v[1] : s == 2 ? v[2] : v[3];
 }
@@ -188,7 +177,7 @@ __global__ __launch_bounds__(256, MINB) void tiled_gemm_kernel(
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const v4i bv = unpack_operand32(pick32(b[tn][s >> 2], s & 3));
+        const v4i bv = codes_operand(pick32(b[tn][s >> 2], s & 3));
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
           acc[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s & 1][tm], bv, acc[tm][tn], 0, 0, 0);

@@ -443,6 +443,9 @@ hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, in
 
 constexpr int kGateupR = 4;  // weight rows per wave in the gate/up GEMV (half gate, half up)
 
+// the gate/up epilogue exists in the one-pass kernel only (K up to 4096 * 4)
+bool gemv_gateup_ok(int64_t K) { return (K + 63) / 64 <= 256; }
+
 // one partial maximum per block: 4 waves x kGateupR/2 output rows
 int64_t gemv_gateup_parts(int64_t N) { return (N + 2 * kGateupR - 1) / (2 * kGateupR); }
 

@@ -24,15 +24,6 @@ namespace bl {
 
 enum { SK_DSTORE = 0, SK_DGATEUP = 1 };
 
-__device__ __forceinline__ v4i dir_unpack(uint32_t w) {
-  v4i r;
-  r[0] = (int)(w & 0x03030303u);
-  r[1] = (int)((w >> 2) & 0x03030303u);
-  r[2] = (int)((w >> 4) & 0x03030303u);
-  r[3] = (int)((w >> 6) & 0x03030303u);
-  return r;
-}
-
 // NBLK: 256-weight blocks per wave (upper bound); XR: 16-byte activation
 // pieces per thread; WPB waves per block.  KS (waves per tile) divides WPB.
 template <int NB, int NBLK, int XR, int WPB, int EPI>
@@ -122,7 +113,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
           uint32_t wd = wv[mat][b][s];
           wd = wok ? wd : 0u;
           acc[mat][s & 1] =
-              __builtin_amdgcn_mfma_i32_16x16x64_i8(av, dir_unpack(wd), acc[mat][s & 1], 0, 0, 0);
+              __builtin_amdgcn_mfma_i32_16x16x64_i8(av, codes_operand(wd), acc[mat][s & 1], 0, 0, 0);
         }
       }
     }

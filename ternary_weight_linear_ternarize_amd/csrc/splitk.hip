@@ -20,15 +20,6 @@
 
 namespace bl {
 
-__device__ __forceinline__ v4i sk_unpack(uint32_t w) {
-  v4i r;
-  r[0] = (int)(w & 0x03030303u);
-  r[1] = (int)((w >> 2) & 0x03030303u);
-  r[2] = (int)((w >> 4) & 0x03030303u);
-  r[3] = (int)((w >> 6) & 0x03030303u);
-  return r;
-}
-
 template <int TMS, int LPR, int WPB>
 __global__ __launch_bounds__(64 * WPB) void mfma_splitk_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
@@ -104,7 +95,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_splitk_kernel(
           // packed word 4 g + s of its weight row
           const int64_t ka = k0 + 256 * b + 64 * g + 16 * s;
           const uint32_t wd = s == 0 ? bw.x : s == 1 ? bw.y : s == 2 ? bw.z : bw.w;
-          const v4i bv = sk_unpack(wd);
+          const v4i bv = codes_operand(wd);
 #pragma unroll
           for (int tm = 0; tm < TMS; ++tm) {
             const int row = 16 * tm + li;

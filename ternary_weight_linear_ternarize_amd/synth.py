@@ -11,6 +11,8 @@ by that constant.  Weight tensors are drawn as ~N(0, 0.02^2), the
 initialisation of the BitLinear listing on the youngju.dev page (section
 "BitNet b1.58"), unless a workload says otherwise.
 """
+import math
+
 import numpy as np
 
 # Workload shapes (M tokens, K in features, N out features).
@@ -103,3 +105,35 @@ def decode_100b(with_weights=True):
 def random_case(seed, M, K, N, w_std=0.02):
     """Small random layer for sweeps over ragged shapes."""
     return {"W": normal(seed, T_W, (N, K), w_std), "X": normal(seed, T_X, (M, K))}
+
+
+def _sum_of_squares(target):
+    """Integers a_i < 2^24 whose squares add up to target (greedy)."""
+    out = []
+    while target > 0:
+        a = math.isqrt(target)
+        out.append(a)
+        target -= a * a
+    assert all(a < 2 ** 24 for a in out)
+    return out
+
+
+def midpoint_rows(D, count, seed):
+    """Rows whose exact mean square sum(x^2) / D equals a number with an odd
+    25-bit significand (a binary32 rounding midpoint), or lies one unit of the
+    integer sum away from it.  Each row is a few nonzero entries a * 2^e with
+    integers a < 2^24 (exact in binary32) at random positions and signs: the
+    integer square sum is chosen first and written as a sum of squares."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for i in range(count):
+        odd = (1 << 24) + 2 * int(rng.integers(0, 1 << 23)) + 1
+        target = D * odd + (0, 1, -1)[i % 3]
+        a = np.array(_sum_of_squares(target), np.float64)
+        row = np.zeros(D, np.float32)
+        pos = rng.choice(D, size=len(a), replace=False)
+        e = int(rng.integers(-40, -10))
+        sign = np.where(rng.random(len(a)) < 0.5, -1.0, 1.0)
+        row[pos] = (sign * np.ldexp(a, e)).astype(np.float32)
+        rows.append(row)
+    return np.stack(rows)

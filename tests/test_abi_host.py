@@ -12,14 +12,15 @@ import pytest
 from ternary_weight_linear_ternarize_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 FAKE = ctypes.c_void_p(0x10000)      # 64 KiB: aligned to anything we check
 ODD = ctypes.c_void_p(0x10001)       # misaligned
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -29,6 +30,7 @@ def test_library_exports_every_declared_function():
     lib = B.lib()
     names = declared_functions()
     assert "bitlinear_pack" in names and "bitnet_ffn_forward" in names
+    assert "bl_probe_read" in names and "bl_probe_empty" in names
     assert len(names) >= 11
     for n in names:
         assert hasattr(lib, n), n
@@ -151,3 +153,78 @@ def test_product_does_not_reference_the_oracle():
                 text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "liboracle" not in text and "orc_" not in text, fn
+
+
+def test_quant_act_requires_the_row_sum():
+    lib = B.lib()
+    assert lib.bitlinear_quant_act(FAKE, 0, 1, 8, FAKE, FAKE, None, None) == B.BL_EINVAL
+
+
+# ----------------------------------------------------------------------------
+# The Python binding checks shapes, dtypes and sizes before any pointer goes
+# to the library (the kernels trust the sizes they are given).  These run on
+# CPU tensors: a well-formed call gets as far as the device check.
+
+def _raises(fn, *words):
+    with pytest.raises(ValueError) as e:
+        fn()
+    msg = str(e.value)
+    assert all(w in msg for w in words), msg
+
+
+def test_binding_rejects_mismatched_forward_arguments():
+    import torch
+    M, K, N = 3, 100, 40
+    kp = B.padded_k(K)
+    Xq = torch.zeros((M, kp), dtype=torch.int8)
+    xs = torch.zeros(M, dtype=torch.float32)
+    rs = torch.zeros(M, dtype=torch.int32)
+    Wp = torch.zeros((N, kp // 16), dtype=torch.int32)
+    sc = torch.zeros(1, dtype=torch.float32)
+    fwd = B.bitlinear_forward
+    _raises(lambda: fwd(Xq, xs, rs, K, Wp, sc, N), "GPU tensor")          # well formed
+    _raises(lambda: fwd(Xq, xs, rs, K + 64, Wp, sc, N), "columns")        # K does not match Xq
+    _raises(lambda: fwd(Xq[:, :64].contiguous(), xs, rs, K, Wp, sc, N), "columns")
+    _raises(lambda: fwd(Xq, xs[:2], rs, K, Wp, sc, N), "x_scale", "shape")
+    _raises(lambda: fwd(Xq, xs, rs.float(), K, Wp, sc, N), "x_rowsum", "dtype")
+    _raises(lambda: fwd(Xq, xs, rs, K, Wp, sc, N + 1), "Wp", "shape")
+    _raises(lambda: fwd(Xq, xs, rs, K, Wp[:, :3].contiguous(), sc, N), "Wp", "shape")
+    _raises(lambda: fwd(Xq.float(), xs, rs, K, Wp, sc, N), "Xq", "dtype")
+    _raises(lambda: fwd(Xq, xs, rs, K, Wp, sc, N, out=torch.zeros((M, N + 1))), "Y", "shape")
+    _raises(lambda: fwd(Xq, xs, rs, K, Wp, sc, N, acc_out=torch.zeros((M, N))), "acc_out", "dtype")
+    _raises(lambda: B.bitlinear_forward_1bit(Xq, xs, rs, K, Wp, sc, N), "Wb", "shape")
+
+
+def test_binding_rejects_mismatched_quant_pack_fused_and_ffn_arguments():
+    import torch
+    M, K, N = 2, 130, 16
+    kp = B.padded_k(K)
+    X = torch.zeros((M, K), dtype=torch.float32)
+    good = (torch.zeros((M, kp), dtype=torch.int8), torch.zeros(M), torch.zeros(M, dtype=torch.int32))
+    _raises(lambda: B.bitlinear_quant_act(X, out=good), "GPU tensor")
+    _raises(lambda: B.bitlinear_quant_act(X.double()), "float32 or bfloat16")
+    _raises(lambda: B.bitlinear_quant_act(X, out=(good[0][:, :64], good[1], good[2])), "Xq", "shape")
+    _raises(lambda: B.bitlinear_quant_act(X, out=(good[0], good[1], good[2][:1])), "x_rowsum")
+    _raises(lambda: B.bitlinear_pack(torch.zeros(N, K), out=torch.zeros((N, 2), dtype=torch.int32)),
+            "Wp", "shape")
+    _raises(lambda: B.bitlinear_pack(torch.zeros(N, K, dtype=torch.float64)), "W", "dtype")
+    Wp = torch.zeros((N, kp // 16), dtype=torch.int32)
+    sc = torch.zeros(1)
+    _raises(lambda: B.bitlinear_forward_fused(X, Wp, sc, N, ws=torch.zeros(8, dtype=torch.uint8)),
+            "ws", "bytes")
+    _raises(lambda: B.bitlinear_forward_fused(X, Wp, sc, N + 1), "Wp", "shape")
+    D, F = K, 48
+    H = torch.zeros((M, D))
+    Wg = torch.zeros((F, kp // 16), dtype=torch.int32)
+    Wd = torch.zeros((D, B.padded_k(F) // 16), dtype=torch.int32)
+    ffn = B.bitnet_ffn_forward
+    _raises(lambda: ffn(H, None, 1e-6, Wg, sc, Wg, sc, Wd, sc, D, F), "GPU tensor")
+    _raises(lambda: ffn(H, None, 1e-6, Wg, sc, Wg, sc, Wd, sc, D + 1, F), "H has")
+    _raises(lambda: ffn(H, None, 1e-6, Wg, sc, Wg, sc, Wg, sc, D, F), "Wd", "shape")
+    _raises(lambda: ffn(H, torch.zeros(D + 1), 1e-6, Wg, sc, Wg, sc, Wd, sc, D, F), "norm_w")
+    _raises(lambda: ffn(H, None, 1e-6, Wg, sc, Wg, sc, Wd, sc, D, F, subln_w=torch.zeros(D)),
+            "subln_w")
+    q = {"q4": good[0], "g4": good[1], "rs4": good[2], "q8": good[0], "g8": good[1], "rs8": good[2]}
+    _raises(lambda: B.bitlinear_forward_a48(q, K, Wp, sc, N), "GPU tensor")
+    q2 = dict(q, rs8=good[2][:1])
+    _raises(lambda: B.bitlinear_forward_a48(q2, K, Wp, sc, N), "x8_rowsum")

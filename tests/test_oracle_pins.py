@@ -441,38 +441,6 @@ def test_rmsnorm_close_to_exact_and_special_rows():
     np.testing.assert_allclose(y, yt, rtol=3e-6, atol=1e-6)
 
 
-def _sum_of_squares(target):
-    """Integers a_i < 2^24 with sum a_i^2 == target (greedy, a handful of terms)."""
-    out = []
-    while target > 0:
-        a = math.isqrt(target)
-        out.append(a)
-        target -= a * a
-    assert all(a < 2 ** 24 for a in out)
-    return out
-
-
-def _midpoint_rows(D, count, seed):
-    """Rows x = a * 2^e whose exact mean square sum(x^2) / D lies exactly on a
-    binary32 rounding midpoint (odd 25-bit significand) or one unit of the sum
-    away from it, so that every rounding step of the mean square is decided
-    by the last bit."""
-    rng = np.random.default_rng(seed)
-    rows = []
-    for i in range(count):
-        odd = (1 << 24) + 2 * int(rng.integers(0, 1 << 23)) + 1  # a midpoint's significand
-        target = D * odd + (0, 1, -1)[i % 3]
-        a = _sum_of_squares(target)
-        row = np.zeros(D, np.float32)
-        pos = rng.choice(D, size=len(a), replace=False)
-        e = int(rng.integers(-40, -10))
-        sign = np.where(rng.random(len(a)) < 0.5, -1.0, 1.0)
-        row[pos] = (sign * np.ldexp(np.array(a, np.float64), e)).astype(np.float32)
-        assert (row[pos].astype(np.float64) == sign * np.ldexp(np.array(a, np.float64), e)).all()
-        rows.append(row)
-    return np.stack(rows)
-
-
 def _rmsnorm_f32(x, g, eps, mean_square=None, scale=None):
     """RMSNorm re-expressed with numpy binary32 scalars: ms = binary32(fsum(x^2)
     / D) (the exact sum rounded once to binary64, a binary64 division, one
@@ -493,7 +461,8 @@ def _rmsnorm_f32(x, g, eps, mean_square=None, scale=None):
 
 def test_rmsnorm_bits_match_an_independent_float32_expression():
     # random rows with a random weight, plus rows whose mean square sits on or
-    # next to a binary32 rounding midpoint (2560 and 6912 wide: the block's D
+    # next to a binary32 rounding midpoint (exact: every entry and square of
+    # synth.midpoint_rows is exact, checked below) (2560 and 6912 wide: the block's D
     # and F, where the division by D is not exact)
     eps = np.float32(np.finfo(np.float32).eps)
     cases = []
@@ -501,7 +470,14 @@ def test_rmsnorm_bits_match_an_independent_float32_expression():
     g = (np.float32(1) + synth.normal(21, 2, (2560,), 0.1)).astype(np.float32)
     cases.append((x, g))
     for D, seed in ((2560, 22), (6912, 23), (64, 24)):
-        xm = _midpoint_rows(D, 60, seed)
+        xm = synth.midpoint_rows(D, 60, seed)
+        for row in xm[:6:3]:  # rows 0 and 3 sit exactly on a midpoint
+            ms = sum((Fraction(float(v)) ** 2 for v in row if v), Fraction(0)) / D
+            assert ms.denominator & (ms.denominator - 1) == 0  # dyadic
+            odd = ms.numerator
+            while odd % 2 == 0:
+                odd //= 2
+            assert odd.bit_length() == 25  # odd 25-bit significand: a binary32 midpoint
         gm = (np.float32(1) + synth.normal(seed, 3, (D,), 0.1)).astype(np.float32)
         cases.append((xm, gm))
     for xc, gc in cases:
