@@ -308,6 +308,31 @@ int bitnet_ffn_forward(const void *H, int dtype, int64_t M, int64_t D, int64_t F
                        const uint32_t *Wd, const float *sd, float *Y, void *ws,
                        size_t ws_bytes, void *stream);
 
+/*
+ * bitnet_ffn_forward_static -- bitnet_ffn_forward for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid device allocation): the same block, bit for bit, with the workspace
+ * taken from a scratch array of BL_FFN_STATIC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends.  It calls no
+ * allocator.  The caller still passes every input and output.
+ *
+ *  Arguments as bitnet_ffn_forward, without ws / ws_bytes.
+ *  Limit: bitnet_ffn_workspace_bytes(M, D, F) <= BL_FFN_STATIC_SCRATCH_BYTES,
+ *         else BL_ESHAPE (e.g. D = 2560, F = 6912 fits up to 64 tokens).
+ *  Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ *  that overlap on one GPU (different streams, or a graph replay running
+ *  beside another call) race; serialise them.  The scratch keeps the last
+ *  call's contents; nothing in it needs to start at zero.
+ *  Errors: as bitnet_ffn_forward, plus BL_ESHAPE for the limit above and
+ *          BL_EHIP if the scratch address cannot be looked up.
+ */
+#define BL_FFN_STATIC_SCRATCH_BYTES (16 << 20)
+int bitnet_ffn_forward_static(const void *H, int dtype, int64_t M, int64_t D, int64_t F,
+                              const float *norm_w, float norm_eps, const float *subln_w,
+                              float subln_eps, const uint32_t *Wg, const float *sg,
+                              const uint32_t *Wu, const float *su, const uint32_t *Wd,
+                              const float *sd, float *Y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,9 @@ def lib():
     L.bitnet_ffn_forward.argtypes = [P, I, I64, I64, I64, P, F, P, F, P, P, P, P, P, P, P, P, SZ,
                                      P]
     L.bitnet_ffn_forward.restype = I
+    L.bitnet_ffn_forward_static.argtypes = [P, I, I64, I64, I64, P, F, P, F, P, P, P, P, P, P,
+                                            P, P]
+    L.bitnet_ffn_forward_static.restype = I
     L.bl_probe_read.argtypes = [P, SZ, I, P, P]
     L.bl_probe_read.restype = I
     L.bl_probe_empty.argtypes = [P]
@@ -399,6 +402,37 @@ def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=No
         _stream(dev))
     _check(st, "bitnet_ffn_forward")
     return Y, ws
+
+
+FFN_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def bitnet_ffn_forward_static(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=None,
+                              subln_w=None, subln_eps=2.0 ** -23):
+    """bitnet_ffn_forward with the library's static per-GPU scratch (no
+    workspace argument, no allocation inside); returns Y [M, D] float32."""
+    M, Dh = _matrix(H, "H")
+    if Dh != D:
+        raise ValueError(f"H has {Dh} columns, D = {D}")
+    dt = _act_dtype(H)
+    dev = H.device
+    Y = out if out is not None else torch.empty((M, D), dtype=torch.float32, device=dev)
+    _check_weights(Wg, sg, F, D, name="Wg")
+    _check_weights(Wu, su, F, D, name="Wu")
+    _check_weights(Wd, sd, D, F, name="Wd")
+    if norm_w is not None:
+        _expect(norm_w, "norm_w", (D,), (torch.float32,))
+    if subln_w is not None:
+        _expect(subln_w, "subln_w", (F,), (torch.float32,))
+    _expect(Y, "Y", (M, D), (torch.float32,))
+    _same_device(H, Wg, sg, Wu, su, Wd, sd, Y, norm_w, subln_w)
+    st = lib().bitnet_ffn_forward_static(
+        _dev(H, "H"), dt, M, D, F, _opt(norm_w, "norm_w"), float(norm_eps),
+        _opt(subln_w, "subln_w"), float(subln_eps), _dev(Wg, "Wg"), _dev(sg, "sg"),
+        _dev(Wu, "Wu"), _dev(su, "su"), _dev(Wd, "Wd"), _dev(sd, "sd"), _dev(Y, "Y"),
+        _stream(dev))
+    _check(st, "bitnet_ffn_forward_static")
+    return Y
 
 
 def ffn_internals(ws, M, D, F):

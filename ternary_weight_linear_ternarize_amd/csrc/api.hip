@@ -4,8 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "bitlinear.h"
 #include "bl_launch.h"
+
+// Scratch of bitnet_ffn_forward_static: one copy per GPU (a file-scope device
+// array lives in the code object loaded on each device), held until the
+// process ends.  In host code this name is only a host-side stand-in: the
+// device address is looked up once per device (static_scratch_address) and
+// only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[BL_FFN_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -26,6 +35,42 @@ int check_forward(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsu
       !aligned(x_rowsum, 4) || !aligned(w_scale, 4))
     return BL_EALIGN;
   return BL_OK;
+}
+
+// Argument checks shared by the two FFN entry points (everything but the
+// workspace).
+int ffn_check(const void* H, int dtype, int64_t M, int64_t D, int64_t F, const float* norm_w,
+              const float* subln_w, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
+              const float* su, const uint32_t* Wd, const float* sd, const float* Y) {
+  if (!H || !Wg || !sg || !Wu || !su || !Wd || !sd || !Y) return BL_EINVAL;
+  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return BL_ESHAPE;
+  if (!aligned(H, dtype == BL_F32 ? 4 : 2) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
+      !aligned(Wd, 16) || !aligned(Y, 4) || !aligned(sg, 4) || !aligned(su, 4) ||
+      !aligned(sd, 4) || (norm_w && !aligned(norm_w, 4)) || (subln_w && !aligned(subln_w, 4)))
+    return BL_EALIGN;
+  return BL_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = reinterpret_cast<char*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -244,23 +289,14 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F) {
   return bitnet_ffn_workspace_layout(M, D, F, nullptr);
 }
 
-int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
-                       const float* norm_w, float norm_eps, const float* subln_w,
-                       float subln_eps, const uint32_t* Wg, const float* sg,
-                       const uint32_t* Wu, const float* su, const uint32_t* Wd, const float* sd,
-                       float* Y, void* ws, size_t ws_bytes, void* stream) {
-  if (!H || !Wg || !sg || !Wu || !su || !Wd || !sd || !Y) return BL_EINVAL;
-  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
-  if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return BL_ESHAPE;
+// The block once its arguments are checked; base is a workspace of at least
+// bitnet_ffn_workspace_bytes(M, D, F) bytes, 256-byte aligned.
+static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
+                   const float* norm_w, float norm_eps, const float* subln_w, float subln_eps,
+                   const uint32_t* Wg, const float* sg, const uint32_t* Wu, const float* su,
+                   const uint32_t* Wd, const float* sd, float* Y, char* base, hipStream_t s) {
   size_t off[BL_FFN_WS_COUNT];
-  const size_t need = bitnet_ffn_workspace_layout(M, D, F, off);
-  if (!ws || ws_bytes < need) return BL_EWORKSPACE;
-  if (!aligned(H, dtype == BL_F32 ? 4 : 2) || !aligned(Wg, 16) || !aligned(Wu, 16) ||
-      !aligned(Wd, 16) || !aligned(Y, 4) || !aligned(ws, 256) || !aligned(sg, 4) ||
-      !aligned(su, 4) || !aligned(sd, 4) || (norm_w && !aligned(norm_w, 4)) ||
-      (subln_w && !aligned(subln_w, 4)))
-    return BL_EALIGN;
-  char* base = reinterpret_cast<char*>(ws);
+  bitnet_ffn_workspace_layout(M, D, F, off);
   float* xn = reinterpret_cast<float*>(base + off[BL_FFN_WS_XN]);
   int8_t* qx = reinterpret_cast<int8_t*>(base + off[BL_FFN_WS_QX]);
   float* gx = reinterpret_cast<float*>(base + off[BL_FFN_WS_GX]);
@@ -272,7 +308,6 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   int32_t* rsh = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_RSH]);
   float* ghp = reinterpret_cast<float*>(base + off[BL_FFN_WS_GHP]);
   int32_t* part = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_PART]);
-  hipStream_t s = as_stream(stream);
   const bool bf16 = dtype == BL_BF16;
 
   // the split-K reduction stores Y in 16-byte vectors; other callers take the
@@ -306,6 +341,34 @@ int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F
   else
     e = bl::launch_mfma(qh, gh, rsh, M, F, Wd, sd, D, Y, nullptr, M > 64, s);
   return hip_status(e);
+}
+
+
+int bitnet_ffn_forward(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
+                       const float* norm_w, float norm_eps, const float* subln_w,
+                       float subln_eps, const uint32_t* Wg, const float* sg,
+                       const uint32_t* Wu, const float* su, const uint32_t* Wd, const float* sd,
+                       float* Y, void* ws, size_t ws_bytes, void* stream) {
+  const int st = ffn_check(H, dtype, M, D, F, norm_w, subln_w, Wg, sg, Wu, su, Wd, sd, Y);
+  if (st != BL_OK) return st;
+  if (!ws || ws_bytes < bitnet_ffn_workspace_bytes(M, D, F)) return BL_EWORKSPACE;
+  if (!aligned(ws, 256)) return BL_EALIGN;
+  return ffn_run(H, dtype, M, D, F, norm_w, norm_eps, subln_w, subln_eps, Wg, sg, Wu, su, Wd, sd,
+                 Y, reinterpret_cast<char*>(ws), as_stream(stream));
+}
+
+int bitnet_ffn_forward_static(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
+                              const float* norm_w, float norm_eps, const float* subln_w,
+                              float subln_eps, const uint32_t* Wg, const float* sg,
+                              const uint32_t* Wu, const float* su, const uint32_t* Wd,
+                              const float* sd, float* Y, void* stream) {
+  const int st = ffn_check(H, dtype, M, D, F, norm_w, subln_w, Wg, sg, Wu, su, Wd, sd, Y);
+  if (st != BL_OK) return st;
+  if (bitnet_ffn_workspace_bytes(M, D, F) > (size_t)BL_FFN_STATIC_SCRATCH_BYTES) return BL_ESHAPE;
+  char* base = nullptr;
+  if (static_scratch_address(&base) != hipSuccess) return BL_EHIP;
+  return ffn_run(H, dtype, M, D, F, norm_w, norm_eps, subln_w, subln_eps, Wg, sg, Wu, su, Wd, sd,
+                 Y, base, as_stream(stream));
 }
 
 }  // extern "C"
