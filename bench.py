@@ -416,7 +416,7 @@ def main():
                                       "GBps": round(alg_dn / (dn_ms * 1e-3) / 1e9, 1)},
         "decode_step_eager_us": round(eager_ms * 1e3, 3),
     }
-    del ups, dns, graph
+    del ups, dns
     torch.cuda.empty_cache()
 
     if not args.no_extra:
