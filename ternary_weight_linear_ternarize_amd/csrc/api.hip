@@ -242,7 +242,7 @@ int bitlinear_forward_fused(const void* X, int dtype, int64_t M, int64_t K, cons
   int32_t* rs = reinterpret_cast<int32_t*>(base + bitlinear_fused_workspace_offset(M, K, 2));
   hipStream_t s = as_stream(stream);
   const bool bf16 = dtype == BL_BF16;
-  if (M == 1 && bl::gemv_fused_ok(K))
+  if (M == 1 && bl::gemv_fused_ok(K, N))
     return hip_status(bl::launch_gemv_fused(X, bf16, K, Wp, w_scale, N, Y, nullptr, xq, xs, rs, s));
   hipError_t e = bl::launch_act_quant(X, bf16, M, K, xq, xs, rs, nullptr, 0, s);
   if (e != hipSuccess) return BL_EHIP;
@@ -326,7 +326,7 @@ static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
   if (subln_w) {
     // SubLN: RMSNorm of h, then its int8 codes
     e = bl::launch_rmsnorm_quant(h, false, M, F, subln_w, subln_eps, hn, qh, gh, rsh, s);
-  } else if (M == 1 && bl::gemv_fused_ok(F)) {
+  } else if (M == 1 && bl::gemv_fused_ok(F, 0)) {
     // requantise h inside the down GEMV (scale from the partial maxima)
     e = bl::launch_gemv_parts(h, ghp, nparts, F, Wd, sd, D, Y, qh, gh, rsh, s);
     return hip_status(e);

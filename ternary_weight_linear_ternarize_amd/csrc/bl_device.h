@@ -132,6 +132,37 @@ __device__ __forceinline__ int quant_code_any(float x, const QuantDiv& q) {
   return q.fast ? quant_code_fast(x, q) : quant_code(x, q.d);
 }
 
+// The rounded, clamped code of x as a float (the same value as quant_code_any).
+__device__ __forceinline__ float quant_value(float x, const QuantDiv& q) {
+  const float a = __fmul_rn(x, kQ);
+  float v;
+  if (q.fast) {
+    const float q0 = __fmul_rn(a, q.y);
+    const float r = __builtin_fmaf(-q0, q.d, a);
+    v = __builtin_fmaf(r, q.y, q0);
+  } else {
+    v = __fdiv_rn(a, q.d);
+  }
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(v), -kQ, kQ);
+}
+
+// Codes of four consecutive values packed as signed bytes (value b in byte b).
+// Each code c in [-127, 127] goes through the unsigned byte c + 128 (exact:
+// an integral float in [1, 255]) and the top bit is flipped back.
+__device__ __forceinline__ uint32_t quant_pack4(float x0, float x1, float x2, float x3,
+                                                const QuantDiv& q) {
+  uint32_t p = __builtin_amdgcn_cvt_pk_u8_f32(__fadd_rn(quant_value(x0, q), 128.0f), 0, 0u);
+  p = __builtin_amdgcn_cvt_pk_u8_f32(__fadd_rn(quant_value(x1, q), 128.0f), 1, p);
+  p = __builtin_amdgcn_cvt_pk_u8_f32(__fadd_rn(quant_value(x2, q), 128.0f), 2, p);
+  p = __builtin_amdgcn_cvt_pk_u8_f32(__fadd_rn(quant_value(x3, q), 128.0f), 3, p);
+  return p ^ 0x80808080u;
+}
+
+// Sum of the four signed bytes of a packed code word, added to acc.
+__device__ __forceinline__ int add_bytes(uint32_t p, int acc) {
+  return __builtin_amdgcn_sdot4((int)p, 0x01010101, acc, false);
+}
+
 // Dequantised output: ((float)acc * (g_w * g_m)) / 127, s = g_w * g_m.
 __device__ __forceinline__ float dequant(int acc, float s) {
   return __fdiv_rn(__fmul_rn((float)acc, s), kQ);

@@ -354,6 +354,240 @@ __global__ __launch_bounds__(256) void gemv_long_kernel(const GemvArgs a) {
   if (rb * R < a.N) gemv_epilogue<R, EPI_STORE>(a, rb, total, rsum, gx, a.s0[0], 0.0f);
 }
 
+// ---------------------------------------------------------------------------
+// Large layers (packed matrix of at least kPipeMinBytes): a streaming form.
+// The grid is one block of 8 waves per CU; wave w walks the row blocks
+// (2 rows each) w, w + T, w + 2T, ... (T = every wave of the grid), issuing
+// the loads of its next row block before the dot products of the current
+// one, so each wave keeps two row blocks (8 KiB at Kp = 8192) in flight for
+// the whole launch instead of one burst per wave.  Every wave runs the same
+// number of iterations, ceil(row blocks / T): rows past N are clamped on load
+// and skipped on store, so the loop is uniform and the loads of one iteration
+// are waited for one by one.
+// The codes of this lane's chunks (lane, lane + 64) stay in registers for
+// the whole launch.  Float activations are quantised once per block into LDS
+// (the block's 512 threads share the row) and then taken into registers.
+constexpr int kPipeWaves = 8;
+constexpr int64_t kPipeMinBytes = 16ll << 20;
+
+template <int KC, int R>
+__device__ __forceinline__ void pipe_issue(const GemvArgs& a, int64_t rb, int lane, int C, int wpr,
+                                           uint4 (&b)[R][KC]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t n = rb * R + r;
+    n = n < a.N ? n : a.N - 1;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      int c = lane + 64 * i;
+      c = c < C ? c : C - 1;
+      b[r][i] = load_stream_u4(reinterpret_cast<const uint4*>(a.W0 + n * wpr) + c);
+    }
+  }
+}
+
+template <int KC, int R>
+__device__ __forceinline__ void pipe_rows(const GemvArgs& a, const uint4 (&b)[R][KC],
+                                          const int (&x)[KC][16], int64_t rb, int rsum,
+                                          float sc) {
+  int part[R];
+  gemv_dots_regs<KC, R>(b, x, part);
+  const int lane = threadIdx.x & 63;
+  const int sum = wave_transpose_reduce<R>(part);
+  const int64_t n = rb * R + gemv_row<R>(lane);
+  // rb past the last row block gives n >= N
+  if (lane < R && n < a.N) {
+    a.Y[n] = dequant(sum - rsum, sc);
+    if (a.acc_out) a.acc_out[n] = sum - rsum;
+  }
+}
+
+// IT > 0: exactly IT iterations, fully unrolled (straight-line code; for
+// float input this measured 0.6 us faster on the 100B-class layer than the
+// loop); IT == 0: the loop over pairs of iterations.
+template <int KC, int XSRC, int IT>
+__global__ __launch_bounds__(64 * kPipeWaves) void gemv_pipe_kernel(const GemvArgs a) {
+  constexpr int R = 2, NW = kPipeWaves, NT = 64 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t gw = (int64_t)blockIdx.x * NW + wave;
+  const int64_t T = (int64_t)gridDim.x * NW;
+  const int C = (int)(a.Kp >> 6), wpr = (int)(a.Kp >> 4);
+  const int64_t nrb = (a.N + R - 1) / R;
+  uint4 bA[R][KC], bB[R][KC];
+  int x[KC][16];
+  int rsum;
+  float gx;
+  if constexpr (XSRC == XS_INT8) {
+    const int8_t* xq = reinterpret_cast<const int8_t*>(a.x);
+    int4 xv[KC][4];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = lane + 64 * i;
+      const int4* p = reinterpret_cast<const int4*>(xq + 64 * (c < C ? c : C - 1));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[i][q] = p[q];
+    }
+    rsum = a.rowsum[0];
+    gx = a.x_scale[0];
+    pipe_issue<KC, R>(a, gw, lane, C, wpr, bA);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const bool ok = lane + 64 * i < C;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[i][4 * q + 0] = ok ? xv[i][q].x : 0;
+        x[i][4 * q + 1] = ok ? xv[i][q].y : 0;
+        x[i][4 * q + 2] = ok ? xv[i][q].z : 0;
+        x[i][4 * q + 3] = ok ? xv[i][q].w : 0;
+      }
+    }
+  } else {
+    __shared__ __attribute__((aligned(16))) int8_t xl[4096 * KC];
+    __shared__ float redf[NW];
+    __shared__ int redi[NW];
+    constexpr int NV = 4096 * KC / 4 / NT;  // groups of 4 values per thread
+    const int K = (int)a.K, ng = (int)(a.Kp >> 2);
+    const bool vec = (reinterpret_cast<uintptr_t>(a.x) & (XSRC == XS_BF16 ? 7 : 15)) == 0;
+    float v[NV][4];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int g = tid + NT * j;
+      if (vec && 4 * g + 3 < K) {
+        if constexpr (XSRC == XS_BF16) {
+          const uint2 u = reinterpret_cast<const uint2*>(a.x)[g];
+          v[j][0] = __uint_as_float(u.x << 16);
+          v[j][1] = __uint_as_float(u.x & 0xffff0000u);
+          v[j][2] = __uint_as_float(u.y << 16);
+          v[j][3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 f = reinterpret_cast<const float4*>(a.x)[g];
+          v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 4 * g + e;
+          v[j][e] = (g < ng && k < K) ? load_act<XSRC == XS_BF16>(a.x, k) : 0.0f;
+        }
+      }
+    }
+    pipe_issue<KC, R>(a, gw, lane, C, wpr, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(v[j][e]));
+    m = block_maxw<NW>(m, redf);
+    const QuantDiv qd = make_qdiv(m);
+    int rs = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int g = tid + NT * j;
+      if (g < ng) {
+        const uint32_t pk = quant_pack4(v[j][0], v[j][1], v[j][2], v[j][3], qd);
+        rs = add_bytes(pk, rs);
+        *reinterpret_cast<uint32_t*>(xl + 4 * g) = pk;
+        if (blockIdx.x == 0 && a.xq_out) reinterpret_cast<uint32_t*>(a.xq_out)[g] = pk;
+      }
+    }
+    rsum = block_sumw<NW>(rs, redi);  // its barrier also publishes xl
+    gx = m;
+    if (blockIdx.x == 0 && tid == 0) {
+      if (a.xs_out) a.xs_out[0] = m;
+      if (a.rs_out) a.rs_out[0] = rsum;
+    }
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+      const int c = lane + 64 * i;
+      const bool ok = c < C;
+      const int4* p = reinterpret_cast<const int4*>(xl + 64 * (ok ? c : 0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int4 t = p[q];
+        x[i][4 * q + 0] = ok ? t.x : 0;
+        x[i][4 * q + 1] = ok ? t.y : 0;
+        x[i][4 * q + 2] = ok ? t.z : 0;
+        x[i][4 * q + 3] = ok ? t.w : 0;
+      }
+    }
+  }
+  const float sc = __fmul_rn(a.s0[0], gx);
+  if constexpr (IT > 0) {
+    uint4 (*buf[2])[KC] = {bA, bB};
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      if (it + 1 < IT)
+        pipe_issue<KC, R>(a, gw + (it + 1) * T, lane, C, wpr,
+                          *reinterpret_cast<uint4(*)[R][KC]>(buf[(it + 1) & 1]));
+      __builtin_amdgcn_sched_barrier(0);
+      pipe_rows<KC, R>(a, *reinterpret_cast<uint4(*)[R][KC]>(buf[it & 1]), x, gw + it * T, rsum,
+                       sc);
+    }
+    return;
+  }
+  // every wave runs the same number of iterations (grid-uniform); bA holds
+  // iteration it on entry to each pair
+  const int64_t ITr = (nrb + T - 1) / T;
+  int64_t rb = gw;
+  for (int64_t p = 0; p < (ITr - 1) / 2; ++p, rb += 2 * T) {
+    pipe_issue<KC, R>(a, rb + T, lane, C, wpr, bB);
+    __builtin_amdgcn_sched_barrier(0);
+    pipe_rows<KC, R>(a, bA, x, rb, rsum, sc);
+    pipe_issue<KC, R>(a, rb + 2 * T, lane, C, wpr, bA);
+    __builtin_amdgcn_sched_barrier(0);
+    pipe_rows<KC, R>(a, bB, x, rb + T, rsum, sc);
+  }
+  if ((ITr & 1) == 0) {  // two iterations left
+    pipe_issue<KC, R>(a, rb + T, lane, C, wpr, bB);
+    __builtin_amdgcn_sched_barrier(0);
+    pipe_rows<KC, R>(a, bA, x, rb, rsum, sc);
+    pipe_rows<KC, R>(a, bB, x, rb + T, rsum, sc);
+  } else {
+    pipe_rows<KC, R>(a, bA, x, rb, rsum, sc);
+  }
+}
+
+// The streaming form for packed matrices of at least 16 MiB with Kp <= 8192.
+static bool pipe_ok(int64_t K, int64_t N) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  return Kp <= 8192 && N * (Kp / 4) >= kPipeMinBytes;
+}
+
+template <int XSRC>
+static hipError_t pipe_launch(const GemvArgs& a, hipStream_t s) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+  }
+  const dim3 grid((unsigned)cus), block(64 * kPipeWaves);
+  const int64_t waves = (int64_t)cus * kPipeWaves, nrb = (a.N + 1) / 2;
+  const int64_t it = (nrb + waves - 1) / waves;
+#define BL_PIPE_IT(KCV)                                                                     \
+  switch (it) {                                                                             \
+    case 1: case 2: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 2>), grid, block, 0, s, a); break; \
+    case 3: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 3>), grid, block, 0, s, a); break; \
+    case 4: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 4>), grid, block, 0, s, a); break; \
+    case 5: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 5>), grid, block, 0, s, a); break; \
+    case 6: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 6>), grid, block, 0, s, a); break; \
+    case 7: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 7>), grid, block, 0, s, a); break; \
+    case 8: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 8>), grid, block, 0, s, a); break; \
+    default: hipLaunchKernelGGL((gemv_pipe_kernel<KCV, XSRC, 0>), grid, block, 0, s, a); break; \
+  }
+  if (a.Kp <= 4096) {
+    BL_PIPE_IT(1)
+  } else {
+    BL_PIPE_IT(2)
+  }
+#undef BL_PIPE_IT
+  return hipGetLastError();
+}
+
 template <int R, int EPI, int XSRC, int NT = 256>
 static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s, int* nblocks = nullptr) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;
@@ -398,15 +632,19 @@ hipError_t launch_gemv(const int8_t* xq, const float* xs, const int32_t* rs, int
   a.x_scale = xs;
   a.rowsum = rs;
   a.acc_out = acc_out;
+  if (pipe_ok(K, N)) return pipe_launch<XS_INT8>(a, s);
   // 2 rows per wave (measured against 4: 6912 -> 2560 3.31 -> 3.15 us,
   // 8192 -> 28672 11.65 -> 11.40 us)
   return gemv_dispatch<2, EPI_STORE, XS_INT8>(a, s);
 }
 
-// The fused kernels redo the row's quantisation in every block; past ~7K
-// inputs that redundant work costs more than a separate quantisation launch
-// (8192 -> 28672: 15.5 us fused, 14.5 us for the quantiser and the int8 GEMV).
-bool gemv_fused_ok(int64_t K) { return (K + 63) / 64 * 64 <= kFusedMaxKp; }
+// The one-burst fused kernels redo the row's quantisation in every block of
+// 2 rows per wave; past ~7K inputs that redundant work costs more than a
+// separate quantisation launch (8192 -> 28672: 15.5 us fused, 14.5 us for the
+// quantiser and the int8 GEMV).  The streaming form quantises once per CU.
+bool gemv_fused_ok(int64_t K, int64_t N) {
+  return (K + 63) / 64 * 64 <= kFusedMaxKp || pipe_ok(K, N);
+}
 
 hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t* Wp,
                              const float* ws, int64_t N, float* Y, int32_t* acc_out,
@@ -417,6 +655,7 @@ hipError_t launch_gemv_fused(const void* X, bool bf16, int64_t K, const uint32_t
   a.xq_out = xq_out;
   a.xs_out = xs_out;
   a.rs_out = rs_out;
+  if (pipe_ok(K, N)) return bf16 ? pipe_launch<XS_BF16>(a, s) : pipe_launch<XS_F32>(a, s);
   // 8 waves per block halve the blocks that each redo the quantisation (2560
   // -> 6912: 3.98 -> 3.58 us); layers with fewer rows take 2 rows per wave
   // so that enough blocks remain (6912 -> 2560: 4.63 -> 3.85 us)

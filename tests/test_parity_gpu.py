@@ -121,6 +121,9 @@ def test_single_layer_512_to_400_all_kernels():
     (2, 64, 16), (3, 16, 63), (5, 65, 64), (8, 1040, 257), (16, 512, 400), (17, 63, 15),
     (31, 1000, 100), (33, 129, 65), (64, 2560, 96), (65, 300, 130), (100, 1040, 257), (129, 64, 129),
     (300, 700, 600),
+    # one token, packed matrix >= 16 MiB (the streaming GEMV), ragged K and odd N
+    (1, 5000, 13301), (1, 4000, 17001), (1, 8192, 16385), (1, 8192, 8192), (1, 8192, 12001),
+    (1, 4096, 40000),
 ])
 def test_random_ragged_shapes(M, K, N):
     d = synth.random_case(1000 + M * 7 + N, M, K, N)
@@ -388,7 +391,12 @@ def test_rmsnorm_on_mean_squares_at_binary32_midpoints(M):
 
 @pytest.mark.parametrize("M,K,N,bf16", [(1, 2560, 6912, False), (1, 6912, 2560, True),
                                         (1, 1, 5, False), (1, 16384, 33, False), (1, 16448, 40, False),
-                                        (1, 8192, 300, True), (3, 700, 130, False), (80, 512, 200, True)])
+                                        (1, 8192, 300, True), (3, 700, 130, False), (80, 512, 200, True),
+                                        # packed matrices of >= 16 MiB: the streaming GEMV
+                                        (1, 8192, 28672, False), (1, 8192, 16400, True),
+                                        (1, 5000, 13301, False), (1, 4000, 17001, True),
+                                        (1, 4097, 16500, False), (1, 8192, 12001, False),
+                                        (1, 4096, 40000, True)])
 def test_forward_fused_from_float(M, K, N, bf16):
     d = synth.random_case(3000 + K + N, M, K, N)
     X = synth.with_outliers(d["X"], synth.outlier_columns(3000 + K, K)) if K > 100 else d["X"]
