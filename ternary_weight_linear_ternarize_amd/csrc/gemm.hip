@@ -294,20 +294,32 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   const int64_t nbase = (int64_t)blockIdx.x * (16 * TPB) + 16 * tile;  // first row of the tile
   const int lr = lane / LPR, lc = lane % LPR;    // load role: row-in-instruction, piece
 
-  // D steps of weights in flight, in registers
+  // D steps of weights in flight, in registers.  Every load is issued
+  // unconditionally (a buffer load): pieces past the row's end (k >= Kw) and
+  // steps past this wave's range get an offset outside the buffer and read as
+  // zero without touching memory.  Zero codes there meet zero activation
+  // bytes (the operand reads below are zeroed for k >= Kp), and with no
+  // branches the compiler waits for one step's loads at a time.
   uint4 st[D][NB][NI];
+  const buf_rsrc wr0 = make_buf_rsrc(W0, (uint32_t)(N * wpr * 4));
+  const buf_rsrc wr1 = make_buf_rsrc(NB == 2 ? W1 : W0, (uint32_t)(N * wpr * 4));
+  uint32_t row_off[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    int64_t n = nbase + RPI * i + lr;
+    n = n < N ? n : N - 1;
+    row_off[i] = (uint32_t)(n * wpr * 4);
+  }
   auto load_step = [&](int sidx, uint4 (&dst)[NB][NI]) {
+    const int c = (s_begin + sidx) * LPR + lc;
+    const bool ok = sidx < nsteps && c < C;
 #pragma unroll
     for (int mat = 0; mat < NB; ++mat) {
-      const uint32_t* W = mat == 0 ? W0 : W1;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        int64_t n = nbase + RPI * i + lr;
-        n = n < N ? n : N - 1;
-        const int c = (s_begin + sidx) * LPR + lc;
-        constexpr uint32_t kPad = BITS == 2 ? 0x55555555u : 0u;  // zero weights / zero bytes
-        dst[mat][i] = c < C ? load_stream_u4(reinterpret_cast<const uint4*>(W + n * wpr) + c)
-                            : make_uint4(kPad, kPad, kPad, kPad);
+        const uint32_t off = ok ? row_off[i] + 16u * (uint32_t)c : 0x80000000u;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(mat == 0 ? wr0 : wr1, off, 0, 2);
+        dst[mat][i] = make_uint4(v[0], v[1], v[2], v[3]);
       }
     }
   };
@@ -324,12 +336,15 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nsteps) load_step(d, st[d]);
-  // activations -> LDS, every load in flight at once
+  // activations -> LDS, every load in flight at once; then the first D steps
+  // of weights, so that waiting for the activations (the older loads) leaves
+  // the weight steps in flight and the loop starts in the state it repeats
   stage_rows_lds<64 * WPB>(Xq, Kp, M, 0, (int)kph, (int)pitch, lds_x);
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_step(d, st[d]);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(D * NB * NI));
   __syncthreads();
 
   v4i acc[NB][2];
@@ -343,10 +358,14 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   for (int sbase = 0; sbase < nsteps; sbase += D) {
 #pragma unroll
   for (int d = 0; d < D; ++d) {
+    // no early exit from this unrolled loop: a step past the end (the last
+    // trip's tail) stages and loads like any other (out-of-range reads are
+    // zero) and skips its dot products, so the loop has one latch and the
+    // compiler keeps the later steps' loads in flight across it
     const int sidx = sbase + d;
-    if (sidx >= nsteps) break;
+    const bool live = sidx < nsteps;  // uniform over the wave (and block)
     const int sabs = s_begin + sidx;
-    if (PH && sabs == next_ph) {
+    if (PH && live && sabs == next_ph) {
       // next phase of the activations (KS == 1 only: every wave of the block
       // is at the same step); the weight patches are wave-private
       __syncthreads();
@@ -359,12 +378,13 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     }
     stage_step(st[d]);
     wave_sync();
-    if (sidx + D < nsteps) load_step(sidx + D, st[d]);
+    load_step(sidx + D, st[d]);
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t k0 = (int64_t)sabs * STEP;
     const int64_t kx = PH ? k0 - xbase : k0;  // k0 within the staged phase
 #pragma unroll
     for (int b = 0; b < STEP / 256; ++b) {
-      if (k0 + 256 * b < Kw) {
+      if (live && k0 + 256 * b < Kw) {
         // this lane's 64 weights of the 256-weight block: 16 bytes of codes
         // or 8 bytes of bits
         uint4 bw[NB];
@@ -531,7 +551,10 @@ static hipError_t stream_go(const int8_t* Xq, const float* xs, const int32_t* rs
   const size_t lds = (size_t)stream_lds_bytes(M, kx, NB, WPB, KS);
   const unsigned blocks = (unsigned)((N + 16 * TPB - 1) / (16 * TPB));
   if (nparts) *nparts = (int)blocks;
-  constexpr int D = 1;  // steps of weights in flight (2 and 4 measured slower: VGPR pressure)
+  // steps of weights in flight per wave: 2 and 3 measured no faster (3 slower)
+  // on the 100B-class layer at 8 and 16 tokens -- the kernel is bound by its
+  // per-wave unpack, LDS operand reads and MFMA chains, not by load latency
+  constexpr int D = 1;
   static bool once =
       (allow_lds(mfma_stream_kernel<NB, kStreamLpr, WPB, D, EPI, KS, BITS, PH>), true);
   (void)once;
