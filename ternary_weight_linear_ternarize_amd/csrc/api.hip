@@ -313,15 +313,22 @@ static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
   // the split-K reduction stores Y in 16-byte vectors; other callers take the
   // single-pass kernels (same bits)
   const bool split = ffn_splitk(M, D, F) && aligned(Y, 16);
-  hipError_t e = bl::launch_rmsnorm_quant(H, bf16, M, D, norm_w, norm_eps, xn, qx, gx, rsx, s);
-  if (e != hipSuccess) return BL_EHIP;
+  hipError_t e;
   int nparts = 0;
-  // one token: the gate/up GEMV while the row fits its K range, else the
-  // MFMA gate/up kernels (which take any K)
-  if (M == 1 && bl::gemv_gateup_ok(D))
-    e = bl::launch_gemv_gateup(qx, gx, rsx, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
-  else
-    e = bl::launch_mfma_gateup(qx, gx, rsx, M, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
+  if (M == 1 && bl::gemv_gateup_norm_ok(D)) {
+    // one token: RMSNorm, quantisation and the gate/up GEMV in one kernel
+    e = bl::launch_gemv_gateup_norm(H, bf16, D, norm_w, norm_eps, Wg, sg, Wu, su, F, h, ghp,
+                                    &nparts, xn, qx, gx, rsx, s);
+  } else {
+    e = bl::launch_rmsnorm_quant(H, bf16, M, D, norm_w, norm_eps, xn, qx, gx, rsx, s);
+    if (e != hipSuccess) return BL_EHIP;
+    // one token: the gate/up GEMV while the row fits its K range, else the
+    // MFMA gate/up kernels (which take any K)
+    if (M == 1 && bl::gemv_gateup_ok(D))
+      e = bl::launch_gemv_gateup(qx, gx, rsx, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
+    else
+      e = bl::launch_mfma_gateup(qx, gx, rsx, M, D, Wg, sg, Wu, su, F, h, ghp, &nparts, s);
+  }
   if (e != hipSuccess) return BL_EHIP;
   if (subln_w) {
     // SubLN: RMSNorm of h, then its int8 codes

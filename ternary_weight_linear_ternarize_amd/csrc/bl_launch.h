@@ -87,6 +87,16 @@ hipError_t launch_gemv_gateup(const int8_t* Xq, const float* x_scale, const int3
                               int64_t K, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
                               hipStream_t s);
+// The same for one token of float hidden state H: RMSNorm (exact mean
+// square), quantisation and the gate/up product in one kernel (every block
+// redoes the norm; block 0 writes xn, the codes, the scale and the row sum).
+// Needs gemv_gateup_norm_ok(K) (padded K <= 4096).
+bool gemv_gateup_norm_ok(int64_t K);
+hipError_t launch_gemv_gateup_norm(const void* H, bool bf16, int64_t K, const float* norm_w,
+                                   float eps, const uint32_t* Wg, const float* sg,
+                                   const uint32_t* Wu, const float* su, int64_t N, float* Hout,
+                                   float* gh_parts, int* nparts, float* xn_out, int8_t* xq_out,
+                                   float* xs_out, int32_t* rs_out, hipStream_t s);
 hipError_t launch_mfma_gateup(const int8_t* Xq, const float* x_scale, const int32_t* rowsum,
                               int64_t M, int64_t K, const uint32_t* Wg, const float* sg,
                               const uint32_t* Wu, const float* su, int64_t N, float* H,

@@ -25,14 +25,18 @@
 //            rne(x * 127 / (scale + 1e-5))), every block redoing the row
 //            (identical bits) into LDS -- one launch per layer;
 //   XS_PARTS float activations whose scale is the maximum of per-block partial
-//            maxima written by the previous kernel (the FFN's h).
+//            maxima written by the previous kernel (the FFN's h);
+//   XS_NF32 / XS_NBF16  float activations RMS-normalised, then quantised, in
+//            every block (the FFN's input: youngju.dev "BitNet b1.58" normalises
+//            before activation_quant) -- the norm, the quantiser and the
+//            gate/up product in one launch.
 #include "bl_device.h"
 #include "bl_launch.h"
 
 namespace bl {
 
 enum { EPI_STORE = 0, EPI_GATEUP = 1 };
-enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3 };
+enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3, XS_NF32 = 4, XS_NBF16 = 5 };
 
 constexpr int kFusedMaxKp = 7168;  // largest padded K quantised inside the GEMV
 
@@ -74,6 +78,9 @@ struct GemvArgs {
   float* Y;
   int32_t* acc_out;         // optional
   float* gh_parts;          // EPI_GATEUP: per-block max |h|
+  const float* norm_w;      // XS_NF32/XS_NBF16: RMSNorm weight (NULL: ones)
+  float eps;                // XS_NF32/XS_NBF16: RMSNorm epsilon
+  float* xn_out;            // XS_NF32/XS_NBF16: optional copy of the normalised row
   int8_t* xq_out;           // fused: optional copy of the codes (block 0)
   float* xs_out;            // fused: optional scale
   int32_t* rs_out;          // fused: optional row sum
@@ -187,6 +194,8 @@ template <int KC, int R, int EPI, int XSRC, int NT>
 __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
   constexpr int RW = (EPI == EPI_GATEUP) ? R / 2 : R;  // output rows per wave
   constexpr bool FUSED = XSRC != XS_INT8;
+  constexpr bool NORM = XSRC == XS_NF32 || XSRC == XS_NBF16;
+  constexpr bool BF = XSRC == XS_BF16 || XSRC == XS_NBF16;
   constexpr int NW = NT / 64;  // waves per block
   __shared__ __attribute__((aligned(16))) int8_t xq_lds[4096 * KC];
   __shared__ float redf[NW];
@@ -217,12 +226,12 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
     if constexpr (XSRC == XS_PARTS) {
       for (int p = tid; p < a.nparts; p += NT) g = fmaxf(g, a.gparts[p]);
     }
-    const bool vec = (reinterpret_cast<uintptr_t>(a.x) & (XSRC == XS_BF16 ? 7 : 15)) == 0;
+    const bool vec = (reinterpret_cast<uintptr_t>(a.x) & (BF ? 7 : 15)) == 0;
 #pragma unroll
     for (int j = 0; j < NWT; ++j) {
       const int wd = tid + NT * j;
       if (vec && 4 * wd + 3 < K) {
-        if constexpr (XSRC == XS_BF16) {
+        if constexpr (BF) {
           const uint2 u = reinterpret_cast<const uint2*>(a.x)[wd];
           xv[j][0] = __uint_as_float(u.x << 16);
           xv[j][1] = __uint_as_float(u.x & 0xffff0000u);
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int k = 4 * wd + b;
-          xv[j][b] = (wd < nw && k < K) ? load_act<XSRC == XS_BF16>(a.x, k) : 0.0f;
+          xv[j][b] = (wd < nw && k < K) ? load_act<BF>(a.x, k) : 0.0f;
         }
       }
     }
@@ -261,6 +270,27 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
   } else {
     // quantise the whole row into LDS (every block does the same, same bits)
     const int nw = (int)(a.Kp >> 2);
+    if constexpr (NORM) {
+      // xn = (x * r) * w, r = 1 / sqrt(ms + eps), ms from the exact sum of
+      // squares (block_meansq); the padding words stay zero
+      __shared__ SumsqScratch sh;
+      const int K = (int)a.K;
+      const float ms = block_meansq<NWT, NT>(xv, a.K, sh);
+      const float r = __fdiv_rn(1.0f, __builtin_sqrtf(__fadd_rn(ms, a.eps)));
+#pragma unroll
+      for (int j = 0; j < NWT; ++j) {
+        const int wd = tid + NT * j;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int k = 4 * wd + b;
+          const bool in = wd < nw && k < K;
+          float v = __fmul_rn(xv[j][b], r);
+          if (a.norm_w) v = __fmul_rn(v, in ? a.norm_w[k] : 0.0f);
+          xv[j][b] = in ? v : 0.0f;
+          if (in && blockIdx.x == 0 && a.xn_out) a.xn_out[k] = v;
+        }
+      }
+    }
     if constexpr (XSRC != XS_PARTS) {
 #pragma unroll
       for (int j = 0; j < NWT; ++j)
@@ -274,13 +304,8 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
     for (int j = 0; j < NWT; ++j) {
       const int wd = tid + NT * j;
       if (wd < nw) {
-        uint32_t pk = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int c = quant_code_any(xv[j][b], qd);
-          rs += c;
-          pk |= ((uint32_t)(c & 0xff)) << (8 * b);
-        }
+        const uint32_t pk = quant_pack4(xv[j][0], xv[j][1], xv[j][2], xv[j][3], qd);
+        rs = add_bytes(pk, rs);
         *reinterpret_cast<uint32_t*>(xq_lds + xslot(wd >> 2) + 4 * (wd & 3)) = pk;
         if (blockIdx.x == 0 && a.xq_out) reinterpret_cast<uint32_t*>(a.xq_out)[wd] = pk;
       }
@@ -603,6 +628,13 @@ static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s, int* nblocks = nullpt
   if (nblocks) *nblocks = (int)blocks;
 #define BL_GEMV_CASE(KCV) \
   hipLaunchKernelGGL((gemv_kernel<KCV, R, EPI, XSRC, NT>), dim3(blocks), dim3(NT), 0, s, a)
+  if constexpr (XSRC == XS_NF32 || XSRC == XS_NBF16) {
+    // the normalising prologue holds the row in registers: one chunk per lane
+    // (92 VGPRs; two chunks take 171)
+    if (C > 64) return hipErrorInvalidValue;
+    BL_GEMV_CASE(1);
+    return hipGetLastError();
+  }
   if (C <= 64) BL_GEMV_CASE(1);
   else if (C <= 128) BL_GEMV_CASE(2);
   else if (C <= 192) BL_GEMV_CASE(3);
@@ -687,6 +719,29 @@ bool gemv_gateup_ok(int64_t K) { return (K + 63) / 64 <= 256; }
 
 // one partial maximum per block: 4 waves x kGateupR/2 output rows
 int64_t gemv_gateup_parts(int64_t N) { return (N + 2 * kGateupR - 1) / (2 * kGateupR); }
+
+bool gemv_gateup_norm_ok(int64_t K) { return (K + 63) / 64 <= 64; }
+
+hipError_t launch_gemv_gateup_norm(const void* H, bool bf16, int64_t K, const float* norm_w,
+                                   float eps, const uint32_t* Wg, const float* sg,
+                                   const uint32_t* Wu, const float* su, int64_t N, float* Hout,
+                                   float* gh_parts, int* nparts, float* xn_out, int8_t* xq_out,
+                                   float* xs_out, int32_t* rs_out, hipStream_t s) {
+  GemvArgs a = base_args(K, Wg, sg, N, Hout);
+  a.x = H;
+  a.W1 = Wu;
+  a.s1 = su;
+  a.gh_parts = gh_parts;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.xn_out = xn_out;
+  a.xq_out = xq_out;
+  a.xs_out = xs_out;
+  a.rs_out = rs_out;
+  // 8-wave blocks: half as many blocks redo the norm as with 4
+  return bf16 ? gemv_dispatch<kGateupR, EPI_GATEUP, XS_NBF16, 512>(a, s, nparts)
+              : gemv_dispatch<kGateupR, EPI_GATEUP, XS_NF32, 512>(a, s, nparts);
+}
 
 hipError_t launch_gemv_gateup(const int8_t* xq, const float* xs, const int32_t* rs, int64_t K,
                               const uint32_t* Wg, const float* sg, const uint32_t* Wu,
