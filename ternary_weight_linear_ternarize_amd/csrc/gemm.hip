@@ -400,9 +400,12 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int64_t ka = k0 + 256 * b + 64 * g + 16 * s;  // this lane's activation bytes
-          v4i a = v4i{0, 0, 0, 0};
-          if (arow && ka < Kp) a = *reinterpret_cast<const v4i*>(xrow + kx + 256 * b + 16 * s);
+          // this lane's activation bytes, read unconditionally: token rows
+          // li >= M read row 0 and only feed result rows that are dropped,
+          // and bytes past Kp (the next staged row, or the weight patches
+          // after the last row) meet weight codes that are zero there --
+          // pieces past the row end load as zero
+          const v4i a = *reinterpret_cast<const v4i*>(xrow + kx + 256 * b + 16 * s);
 #pragma unroll
           for (int mat = 0; mat < NB; ++mat) {
             v4i bv;
