@@ -250,10 +250,13 @@ int bitlinear_forward_fused(const void* X, int dtype, int64_t M, int64_t K, cons
   return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
 }
 
-// Batches of 17..64 tokens run the FFN's down projection (few weight rows,
-// long K) as a split-K GEMM.
+// Batches of 17..48 tokens run the FFN's down projection (few weight rows,
+// long K) as a split-K GEMM; from about 48 tokens on the single-pass GEMM
+// with 4 chunks of loads in flight is faster (the 2B-class block at 32
+// tokens 29.3 us split against 31.2 single-pass, at 64 tokens 34.9 against
+// 33.2).
 static bool ffn_splitk(int64_t M, int64_t D, int64_t F) {
-  return M >= 17 && M <= 64 && bl::splitk_plan(M, F, D).ok;
+  return M >= 17 && M <= 48 && bl::splitk_plan(M, F, D).ok;
 }
 
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off) {

@@ -41,11 +41,7 @@ hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, i
 constexpr int kChunk = 256;         // K per chunk
 constexpr int kLdsPitch = 256 + 16; // bytes per staged activation row
 
-__device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
-  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
-}
-
-template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
+template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI, int P>
 __global__ __launch_bounds__(256) void mfma_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp,
@@ -69,59 +65,50 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
   const int64_t wpr = Kp / 16;
   const int64_t nchunks = (Kp + kChunk - 1) / kChunk;
 
-  // ---- loaders
-  uint4 a_reg[A_U4_PAD];
-  auto load_a = [&](int64_t kc) {
-    if constexpr (A_U4 > 0) {
+  // ---- loaders: P chunks of loads in flight, in registers.  Buffer loads
+  // issued without branches: rows past M, words past a row's end and chunks
+  // past K read as zero (zero codes, zero activations), so the compiler
+  // waits for one chunk's loads at a time.
+  static_assert(P >= 1, "at least one chunk in flight");
+  const int64_t mrows = M - m0 < BM ? M - m0 : BM;  // rows of this block
+  const int64_t nrows = N - n0 < BN ? N - n0 : BN;
+  const buf_rsrc ra = make_buf_rsrc(Xq + m0 * Kp, (uint32_t)(mrows * Kp));
+  const buf_rsrc rb0 = make_buf_rsrc(W0 + n0 * wpr, (uint32_t)(nrows * wpr * 4));
+  const buf_rsrc rb1 = make_buf_rsrc((NB == 2 ? W1 : W0) + n0 * wpr, (uint32_t)(nrows * wpr * 4));
+  u32x4 a_reg[P][A_U4_PAD];
+  u32x4 b_reg[P][NB][TN];
+  auto load = [&](int64_t c, int slot) {
+    const int64_t kc = c * kChunk;
 #pragma unroll
-      for (int i = 0; i < A_U4; ++i) {
-        const int u = tid + 256 * i;
-        const int row = u >> 4, c16 = u & 15;
-        const int64_t m = m0 + row, k = kc + 16 * c16;
-        if (m < M && k < Kp)
-          a_reg[i] = *reinterpret_cast<const uint4*>(Xq + m * Kp + k);
-        else
-          a_reg[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    } else {
-      // fewer than 256 uint4 per chunk: threads beyond BM*16 idle
-      const int u = tid;
+    for (int i = 0; i < A_U4_PAD; ++i) {
+      const int u = tid + 256 * i;
       const int row = u >> 4, c16 = u & 15;
-      const int64_t m = m0 + row, k = kc + 16 * c16;
-      if (row < BM && m < M && k < Kp)
-        a_reg[0] = *reinterpret_cast<const uint4*>(Xq + m * Kp + k);
-      else
-        a_reg[0] = make_uint4(0u, 0u, 0u, 0u);
+      const int64_t k = kc + 16 * c16;
+      const bool ok = row < BM && row < mrows && k < Kp;
+      a_reg[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(
+          ra, ok ? (uint32_t)(row * Kp + k) : 0x80000000u, 0, 0);
     }
-  };
-  auto store_a = [&](int buf) {
-    if constexpr (A_U4 > 0) {
-#pragma unroll
-      for (int i = 0; i < A_U4; ++i) {
-        const int u = tid + 256 * i;
-        const int row = u >> 4, c16 = u & 15;
-        *reinterpret_cast<uint4*>(&lds_a[buf][row * kLdsPitch + 16 * c16]) = a_reg[i];
-      }
-    } else {
-      const int u = tid;
-      const int row = u >> 4, c16 = u & 15;
-      if (row < BM) *reinterpret_cast<uint4*>(&lds_a[buf][row * kLdsPitch + 16 * c16]) = a_reg[0];
-    }
-  };
-  uint4 b_reg[NB][TN];
-  auto load_b = [&](int64_t kc) {
+    const int64_t word = kc / 16 + 4 * g;
 #pragma unroll
     for (int mat = 0; mat < NB; ++mat) {
-      const uint32_t* W = (mat == 0) ? W0 : W1;
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int64_t n = n0 + 16 * (wn * TN + tn) + li;
-        const int64_t word = kc / 16 + 4 * g;
-        if (n < N && word < wpr)
-          b_reg[mat][tn] = *reinterpret_cast<const uint4*>(W + n * wpr + word);
-        else
-          b_reg[mat][tn] = make_uint4(0u, 0u, 0u, 0u);
+        // rows past N are past the resource's range and read as zero; the
+        // weights are cached (the WAVES_M waves and the row blocks of the
+        // grid read them again)
+        const int64_t nl = 16 * (wn * TN + tn) + li;
+        b_reg[slot][mat][tn] = __builtin_amdgcn_raw_buffer_load_b128(
+            mat == 0 ? rb0 : rb1, word < wpr ? (uint32_t)((nl * wpr + word) * 4) : 0x80000000u, 0, 0);
       }
+    }
+  };
+  auto store_a = [&](int buf, int slot) {
+#pragma unroll
+    for (int i = 0; i < A_U4_PAD; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u >> 4, c16 = u & 15;
+      if (A_U4 > 0 || row < BM)
+        *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsPitch + 16 * c16]) = a_reg[slot][i];
     }
   };
 
@@ -133,39 +120,48 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) acc[mat][tm][tn] = v4i{0, 0, 0, 0};
 
-  load_a(0);
-  load_b(0);
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int buf = (int)(c & 1);
-    store_a(buf);
-    uint4 b_cur[NB][TN];
 #pragma unroll
-    for (int mat = 0; mat < NB; ++mat)
+  for (int d = 0; d < P; ++d) {
+    load(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t cb = 0; cb < nchunks; cb += P) {
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) b_cur[mat][tn] = b_reg[mat][tn];
-    __syncthreads();
-    if (c + 1 < nchunks) {
-      load_a((c + 1) * kChunk);
-      load_b((c + 1) * kChunk);
-    }
-    const int8_t* la = &lds_a[buf][0];
+    for (int d = 0; d < P; ++d) {
+      const int64_t c = cb + d;
+      const bool live = c < nchunks;  // uniform
+      const int buf = (int)(c & 1);
+      if (live) store_a(buf, d);
+      u32x4 b_cur[NB][TN];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      v4i a[TM];
+      for (int mat = 0; mat < NB; ++mat)
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int row = 16 * (wm * TM + tm) + li;
-        a[tm] = *reinterpret_cast<const v4i*>(la + row * kLdsPitch + 64 * g + 16 * s);
-      }
+        for (int tn = 0; tn < TN; ++tn) b_cur[mat][tn] = b_reg[d][mat][tn];
+      if (live) __syncthreads();
+      // refill the slot with chunk c + P (zeros past the end), then compute
+      load(c + P, d);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) {
+        const int8_t* la = &lds_a[buf][0];
 #pragma unroll
-      for (int mat = 0; mat < NB; ++mat) {
+        for (int s = 0; s < 4; ++s) {
+          v4i a[TM];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const v4i b = codes_operand(pick(b_cur[mat][tn], s));
+          for (int tm = 0; tm < TM; ++tm) {
+            const int row = 16 * (wm * TM + tm) + li;
+            a[tm] = *reinterpret_cast<const v4i*>(la + row * kLdsPitch + 64 * g + 16 * s);
+          }
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
-            acc[mat][tm][tn] =
-                __builtin_amdgcn_mfma_i32_16x16x64_i8(a[tm], b, acc[mat][tm][tn], 0, 0, 0);
+          for (int mat = 0; mat < NB; ++mat) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+              const v4i b = codes_operand(b_cur[mat][tn][s]);
+#pragma unroll
+              for (int tm = 0; tm < TM; ++tm)
+                acc[mat][tm][tn] =
+                    __builtin_amdgcn_mfma_i32_16x16x64_i8(a[tm], b, acc[mat][tm][tn], 0, 0, 0);
+            }
+          }
         }
       }
     }
@@ -616,7 +612,7 @@ static hipError_t stream_launch(const int8_t* Xq, const float* xs, const int32_t
 #undef BL_STREAM_GO
 }
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
+template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI, int P = 1>
 static hipError_t mfma_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                               int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
                               const float* s1, int64_t N, float* Y, int32_t* acc_out,
@@ -625,7 +621,7 @@ static hipError_t mfma_launch(const int8_t* Xq, const float* xs, const int32_t* 
   constexpr int BN = 16 * TN * WAVES_N;
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   if (nparts) *nparts = (int)nbn;
-  hipLaunchKernelGGL((mfma_gemm_kernel<TM, TN, WAVES_M, WAVES_N, EPI>), dim3((unsigned)(nbm * nbn)),
+  hipLaunchKernelGGL((mfma_gemm_kernel<TM, TN, WAVES_M, WAVES_N, EPI, P>), dim3((unsigned)(nbm * nbn)),
                      dim3(256), 0, s, Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts,
                      (int)nbn);
   return hipGetLastError();
@@ -648,9 +644,16 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
   // 17 <= M <= 64: 32 x 32 block tiles (four 16 x 16 wave tiles) keep more
-  // blocks in flight than 64-row tiles for these weight-streaming shapes
-  return mfma_launch<1, 1, 2, 2, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
-                                           acc_out, nullptr, nullptr, s);
+  // blocks in flight than 64-row tiles for these weight-streaming shapes.
+  // Loads of 4 chunks in flight for long K (and at up to 32 tokens), else 2:
+  // at 64 tokens 2560 -> 6912 took 9.5 us with 2 against 10.5 with 4 and
+  // 10.2 with 1, 6912 -> 2560 13.3 us with 4 against 16.5 with 2 and 19.5
+  // with 1
+  if (M <= 32 || (Kp + kChunk - 1) / kChunk >= 16)
+    return mfma_launch<1, 1, 2, 2, MF_STORE, 4>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                                acc_out, nullptr, nullptr, s);
+  return mfma_launch<1, 1, 2, 2, MF_STORE, 2>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                              acc_out, nullptr, nullptr, s);
 }
 
 // The stacked a4.8 product (M2 = 2 Mh code rows) where launch_mfma runs the
@@ -701,10 +704,12 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                               gh_parts, nparts, s);
-  // 17 <= M <= 64: 64 x 16 block tiles (waves split the token rows)
+  // 17 <= M <= 64: 32 x 32 block tiles with 2 chunks of loads in flight
+  // (the FFN at 64 tokens 35.2 us against 38.2 with 64 x 16 tiles and one
+  // chunk in flight, at 32 tokens 28.7 against 33.7)
   if (M <= 64)
-    return mfma_launch<1, 1, 4, 1, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
-                                              gh_parts, nparts, s);
+    return mfma_launch<1, 1, 2, 2, MF_GATEUP, 2>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                                 gh_parts, nparts, s);
   return mfma_launch<4, 4, 2, 2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                             gh_parts, nparts, s);
 }

@@ -121,6 +121,9 @@ def test_single_layer_512_to_400_all_kernels():
     (2, 64, 16), (3, 16, 63), (5, 65, 64), (8, 1040, 257), (16, 512, 400), (17, 63, 15),
     (31, 1000, 100), (33, 129, 65), (64, 2560, 96), (65, 300, 130), (100, 1040, 257), (129, 64, 129),
     (300, 700, 600),
+    # 17..64 tokens on the skinny tiled GEMM with 2 or 4 chunks of loads in
+    # flight: partial last chunks, chunk counts not multiples of the depth
+    (48, 3000, 77), (64, 4100, 50), (20, 8000, 33), (64, 7000, 40), (64, 9000, 20),
     # one token, packed matrix >= 16 MiB (the streaming GEMV), ragged K and odd N
     (1, 5000, 13301), (1, 4000, 17001), (1, 8192, 16385), (1, 8192, 8192), (1, 8192, 12001),
     (1, 4096, 40000),
