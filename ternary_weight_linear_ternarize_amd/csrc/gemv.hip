@@ -39,6 +39,7 @@ enum { EPI_STORE = 0, EPI_GATEUP = 1 };
 enum { XS_INT8 = 0, XS_F32 = 1, XS_BF16 = 2, XS_PARTS = 3, XS_NF32 = 4, XS_NBF16 = 5 };
 
 constexpr int kFusedMaxKp = 7168;  // largest padded K quantised inside the GEMV
+constexpr int kGpPerThread = 2;     // XS_PARTS: partial maxima loaded per thread up front
 
 // Block maximum (non-negative values) / sum over NW waves; red holds NW slots.
 template <int NW>
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
   int4 xi[NXI];
   float xv[NWT][4];
   float g = 0.0f;
+  uint32_t gp[kGpPerThread] = {};  // XS_PARTS: partial maxima (float bits)
   if constexpr (!FUSED) {
     const int4* xg = reinterpret_cast<const int4*>(a.x);
 #pragma unroll
@@ -224,7 +226,14 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
   } else {
     const int K = (int)a.K, nw = (int)(a.Kp >> 2);
     if constexpr (XSRC == XS_PARTS) {
-      for (int p = tid; p < a.nparts; p += NT) g = fmaxf(g, a.gparts[p]);
+      // the partial maxima: branch-free loads of kGpPerThread per thread
+      // (past nparts they read 0), so they are in flight together with the
+      // row and the weights instead of ahead of them; any beyond that in a loop
+      const buf_rsrc rg = make_buf_rsrc(a.gparts, (uint32_t)(4 * a.nparts));
+#pragma unroll
+      for (int i = 0; i < kGpPerThread; ++i)
+        gp[i] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(4 * (tid + NT * i)), 0, 0);
+      for (int p = tid + NT * kGpPerThread; p < a.nparts; p += NT) g = fmaxf(g, a.gparts[p]);
     }
     const bool vec = (reinterpret_cast<uintptr_t>(a.x) & (BF ? 7 : 15)) == 0;
 #pragma unroll
@@ -296,6 +305,9 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
       for (int j = 0; j < NWT; ++j)
 #pragma unroll
         for (int b = 0; b < 4; ++b) g = fmaxf(g, fabsf(xv[j][b]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kGpPerThread; ++i) g = fmaxf(g, __uint_as_float(gp[i]));
     }
     g = block_maxw<NW>(g, redf);
     const QuantDiv qd = make_qdiv(g);

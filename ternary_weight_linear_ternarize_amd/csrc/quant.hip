@@ -122,8 +122,18 @@ __global__ __launch_bounds__(NT) void act_quant_kernel(const void* __restrict__ 
   const int64_t m = blockIdx.x;
   const char* base = reinterpret_cast<const char*>(X) + m * K * (BF16 ? 2 : 4);
   float g = 0.0f;
+  // partial maxima: the first kAqParts per thread as branch-free loads issued
+  // with the row's loads (both in flight at once), any beyond in a loop
+  constexpr int kAqParts = 2;
+  uint32_t gp[kAqParts] = {};
   if (gamma_parts) {
-    for (int p = threadIdx.x; p < nparts; p += blockDim.x) g = fmaxf(g, gamma_parts[(int64_t)p * M + m]);
+    const buf_rsrc rg = make_buf_rsrc(gamma_parts, (uint32_t)(4 * nparts * M));
+#pragma unroll
+    for (int i = 0; i < kAqParts; ++i) {
+      const int p = threadIdx.x + NT * i;
+      gp[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rg, p < nparts ? (uint32_t)(4 * ((int64_t)p * M + m)) : 0x80000000u, 0, 0);
+    }
   }
   int rs;
   if constexpr (NWT > 0) {
@@ -134,12 +144,22 @@ __global__ __launch_bounds__(NT) void act_quant_kernel(const void* __restrict__ 
       for (int j = 0; j < NWT; ++j)
 #pragma unroll
         for (int b = 0; b < 4; ++b) g = fmaxf(g, fabsf(xv[j][b]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kAqParts; ++i) g = fmaxf(g, __uint_as_float(gp[i]));
+      for (int p = threadIdx.x + NT * kAqParts; p < nparts; p += NT)
+        g = fmaxf(g, gamma_parts[(int64_t)p * M + m]);
     }
     g = block_max(g, redf);
     rs = store_row_codes<NWT, NT>(xv, Kp / 4, make_qdiv(g), Xq + m * Kp);
   } else {
     if (!gamma_parts) {
       for (int64_t k = threadIdx.x; k < K; k += blockDim.x) g = fmaxf(g, fabsf(load_act<BF16>(base, k)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kAqParts; ++i) g = fmaxf(g, __uint_as_float(gp[i]));
+      for (int p = threadIdx.x + NT * kAqParts; p < nparts; p += NT)
+        g = fmaxf(g, gamma_parts[(int64_t)p * M + m]);
     }
     g = block_max(g, redf);
     rs = write_codes([&](int64_t k) { return load_act<BF16>(base, k); }, K, Kp, make_qdiv(g),
