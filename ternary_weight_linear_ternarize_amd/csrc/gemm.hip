@@ -696,11 +696,14 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
                               hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (direct_ok(M, K, N, 2))
-    return launch_direct_gateup(Xq, xs, rs, M, K, Wg, sg, Wu, su, N, H, gh_parts, nparts, s);
+  // the streaming kernel first: the 2B-class FFN block 20.4-20.8 -> 20.2-20.4
+  // us at 8 tokens, 18.4-18.8 -> 18.2-18.3 at 2, 22.0-22.6 -> 22.0-22.4 at 16
+  // against the direct kernel (two boxes)
   if (stream_ok(M, Kp))
     return stream_launch<2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr, gh_parts,
                                        nparts, s);
+  if (direct_ok(M, K, N, 2))
+    return launch_direct_gateup(Xq, xs, rs, M, K, Wg, sg, Wu, su, N, H, gh_parts, nparts, s);
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                               gh_parts, nparts, s);
