@@ -266,12 +266,10 @@ int bitlinear_forward_fused(const void *X, int dtype, int64_t M, int64_t K, cons
  *   HN  float [M][F]   RMSNorm(h) (written only with SubLN)
  *   GH  float [M]      max |h| per token (stored as float bits)
  *   QH  int8  [M][Fp]  int8 codes of h;  RSH int32 [M] row sums
- *   GHP float [P][M]   per-block partial maxima of |h| (scratch)
- *   PART int32         split-K partial sums of the down projection for
- *                      17..48 tokens (scratch; size 0 otherwise)           */
+ *   GHP float [P][M]   per-block partial maxima of |h| (scratch)          */
 enum {
     BL_FFN_WS_XN = 0, BL_FFN_WS_QX, BL_FFN_WS_GX, BL_FFN_WS_RSX, BL_FFN_WS_H, BL_FFN_WS_HN,
-    BL_FFN_WS_GH, BL_FFN_WS_QH, BL_FFN_WS_RSH, BL_FFN_WS_GHP, BL_FFN_WS_PART, BL_FFN_WS_COUNT
+    BL_FFN_WS_GH, BL_FFN_WS_QH, BL_FFN_WS_RSH, BL_FFN_WS_GHP, BL_FFN_WS_COUNT
 };
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t *off);
 size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F);
@@ -295,9 +293,7 @@ size_t bitnet_ffn_workspace_bytes(int64_t M, int64_t D, int64_t F);
  *           the 2B-class FFN workload states it).  subln_eps: its epsilon.
  *  Wg, Wu   [F][Dp/16] packed (16-byte aligned), sg, su their scales.
  *  Wd       [D][Fp/16] packed, sd its scale.
- *  Y        [M][D] float32, device, 4-byte aligned, written (16-byte
- *           alignment lets 17..48 tokens take the split-K down projection;
- *           the result is the same either way).
+ *  Y        [M][D] float32, device, 4-byte aligned, written.
  *  ws       >= bitnet_ffn_workspace_bytes(M, D, F) bytes, 256-byte aligned.
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP.
  */

@@ -17,7 +17,7 @@ BL_OK, BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EWORKSPACE, BL_EHIP = range(6)
 BL_TERNARY, BL_BINARY, BL_BINARY_1BIT = 0, 1, 2
 BL_F32, BL_BF16 = 0, 1
 BL_KERNEL_AUTO, BL_KERNEL_GEMV, BL_KERNEL_SKINNY, BL_KERNEL_TILED = range(4)
-FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "HN", "GH", "QH", "RSH", "GHP", "PART")
+FFN_WS_NAMES = ("XN", "QX", "GX", "RSX", "H", "HN", "GH", "QH", "RSH", "GHP")
 
 _lib = None
 

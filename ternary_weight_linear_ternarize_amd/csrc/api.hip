@@ -250,23 +250,12 @@ int bitlinear_forward_fused(const void* X, int dtype, int64_t M, int64_t K, cons
   return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
 }
 
-// Batches of 17..48 tokens run the FFN's down projection (few weight rows,
-// long K) as a split-K GEMM; from about 48 tokens on the single-pass GEMM
-// with 4 chunks of loads in flight is faster (the 2B-class block at 32
-// tokens 29.3 us split against 31.2 single-pass, at 64 tokens 34.9 against
-// 33.2).
-static bool ffn_splitk(int64_t M, int64_t D, int64_t F) {
-  return M >= 17 && M <= 48 && bl::splitk_plan(M, F, D).ok;
-}
-
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off) {
   if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return 0;
   const size_t m = (size_t)M;
   int64_t parts = bl::gemv_gateup_parts(F);
   const int64_t p2 = bl::mfma_gateup_parts(M, F);
   if (p2 > parts) parts = p2;
-  // split-K partial sums of the down projection (batches of 17..64 tokens)
-  const size_t part = ffn_splitk(M, D, F) ? (size_t)bl::splitk_plan(M, F, D).part_elems * 4 : 0;
   const size_t sizes[BL_FFN_WS_COUNT] = {
       m * (size_t)D * 4,       // XN
       m * (size_t)padk(D),     // QX
@@ -278,7 +267,6 @@ size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off)
       m * (size_t)padk(F),     // QH
       m * 4,                   // RSH
       m * (size_t)parts * 4,   // GHP
-      part,                    // PART
   };
   size_t o = 0;
   for (int i = 0; i < BL_FFN_WS_COUNT; ++i) {
@@ -310,12 +298,8 @@ static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
   int8_t* qh = reinterpret_cast<int8_t*>(base + off[BL_FFN_WS_QH]);
   int32_t* rsh = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_RSH]);
   float* ghp = reinterpret_cast<float*>(base + off[BL_FFN_WS_GHP]);
-  int32_t* part = reinterpret_cast<int32_t*>(base + off[BL_FFN_WS_PART]);
   const bool bf16 = dtype == BL_BF16;
 
-  // the split-K reduction stores Y in 16-byte vectors; other callers take the
-  // single-pass kernels (same bits)
-  const bool split = ffn_splitk(M, D, F) && aligned(Y, 16);
   hipError_t e;
   int nparts = 0;
   if (M == 1 && bl::gemv_gateup_norm_ok(D)) {
@@ -346,8 +330,6 @@ static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
   if (e != hipSuccess) return BL_EHIP;
   if (M == 1)
     e = bl::launch_gemv(qh, gh, rsh, F, Wd, sd, D, Y, nullptr, s);
-  else if (split)
-    e = bl::launch_splitk(qh, gh, rsh, M, F, Wd, sd, D, Y, part, s);
   else
     e = bl::launch_mfma(qh, gh, rsh, M, F, Wd, sd, D, Y, nullptr, M > 64, s);
   return hip_status(e);

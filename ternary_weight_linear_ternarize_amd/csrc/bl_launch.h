@@ -121,19 +121,6 @@ hipError_t launch_direct_gateup(const int8_t* Xq, const float* x_scale, const in
                                 const uint32_t* Wu, const float* su, int64_t N, float* H,
                                 float* gh_parts, int* nparts, hipStream_t s);
 
-// Split-K skinny GEMM for 1 <= M <= 64 (splitk.hip): grid = ntb weight-row
-// blocks x ksb K parts; with ksb > 1 the int32 partial sums go to `part`
-// (part_elems int32) and a second kernel adds them and dequantises.  ok is
-// false when the shape is not covered (N % 4 != 0, M > 64, LDS).
-struct SplitPlan {
-  int64_t ntb, ksb, part_elems;
-  bool ok;
-};
-SplitPlan splitk_plan(int64_t M, int64_t K, int64_t N);
-hipError_t launch_splitk(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,
-                         int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
-                         int32_t* part, hipStream_t s);
-
 // Upper bounds of the partial-maximum slots per row the gate/up kernels write.
 int64_t gemv_gateup_parts(int64_t N);
 int64_t mfma_gateup_parts(int64_t M, int64_t N);

@@ -41,29 +41,41 @@ hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, i
 constexpr int kChunk = 256;         // K per chunk
 constexpr int kLdsPitch = 256 + 16; // bytes per staged activation row
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI, int P>
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(
+// KS > 1 splits K inside the block: KS groups of the 4 waves, group kg taking
+// chunks kg, kg + KS, ... of the same tile (each group its own LDS stages),
+// and the groups' partial accumulators are added through LDS before the
+// epilogue -- KS times as many waves in flight for layers with few output
+// tiles and long K (the FFN's down projection: 6912 -> 2560 at 64 tokens,
+// 160 tiles of 32 x 32).  This replaced a split-K kernel whose int32
+// partials went through the workspace to a second launch: the FFN at 17
+// to 48 tokens measured 27.7-29.9 us this way against 27.6-32.7 us.
+template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI, int P, int KS = 1>
+__global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp,
     const uint32_t* __restrict__ W0, const float* __restrict__ s0,
     const uint32_t* __restrict__ W1, const float* __restrict__ s1, int64_t N,
     float* __restrict__ Y, int32_t* __restrict__ acc_out, float* __restrict__ gh_parts,
     int nbn) {
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves per block");
+  static_assert(WAVES_M * WAVES_N == 4, "4 waves per K group");
+  constexpr int NT = 256 * KS;
   constexpr int BM = 16 * TM * WAVES_M;
   constexpr int BN = 16 * TN * WAVES_N;
   constexpr int NB = (EPI == MF_GATEUP) ? 2 : 1;       // weight matrices
   constexpr int A_U4 = BM * (kChunk / 16) / 256;       // uint4 per thread per chunk
   constexpr int A_U4_PAD = A_U4 > 0 ? A_U4 : 1;
-  __shared__ __attribute__((aligned(16))) int8_t lds_a[2][BM * kLdsPitch];
+  __shared__ __attribute__((aligned(16))) int8_t lds_a[2][KS][BM * kLdsPitch];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int kg = wave >> 2, wl = wave & 3;           // K group, wave within it
+  const int gtid = tid & 255;                        // thread within the K group
+  const int wm = wl / WAVES_N, wn = wl % WAVES_N;
   const int g = lane >> 4, li = lane & 15;
   const int bn = blockIdx.x % nbn, bm = blockIdx.x / nbn;
   const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
   const int64_t wpr = Kp / 16;
   const int64_t nchunks = (Kp + kChunk - 1) / kChunk;
+  const int64_t nsteps = (nchunks + KS - 1) / KS;    // chunks per K group (upper bound)
 
   // ---- loaders: P chunks of loads in flight, in registers.  Buffer loads
   // issued without branches: rows past M, words past a row's end and chunks
@@ -77,11 +89,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
   const buf_rsrc rb1 = make_buf_rsrc((NB == 2 ? W1 : W0) + n0 * wpr, (uint32_t)(nrows * wpr * 4));
   u32x4 a_reg[P][A_U4_PAD];
   u32x4 b_reg[P][NB][TN];
-  auto load = [&](int64_t c, int slot) {
-    const int64_t kc = c * kChunk;
+  // step t of group kg is chunk t * KS + kg
+  auto load = [&](int64_t t, int slot) {
+    const int64_t kc = (t * KS + kg) * kChunk;
 #pragma unroll
     for (int i = 0; i < A_U4_PAD; ++i) {
-      const int u = tid + 256 * i;
+      const int u = gtid + 256 * i;
       const int row = u >> 4, c16 = u & 15;
       const int64_t k = kc + 16 * c16;
       const bool ok = row < BM && row < mrows && k < Kp;
@@ -105,10 +118,10 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
   auto store_a = [&](int buf, int slot) {
 #pragma unroll
     for (int i = 0; i < A_U4_PAD; ++i) {
-      const int u = tid + 256 * i;
+      const int u = gtid + 256 * i;
       const int row = u >> 4, c16 = u & 15;
       if (A_U4 > 0 || row < BM)
-        *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsPitch + 16 * c16]) = a_reg[slot][i];
+        *reinterpret_cast<u32x4*>(&lds_a[buf][kg][row * kLdsPitch + 16 * c16]) = a_reg[slot][i];
     }
   };
 
@@ -125,12 +138,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
     load(d, d);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int64_t cb = 0; cb < nchunks; cb += P) {
+  for (int64_t tb = 0; tb < nsteps; tb += P) {
 #pragma unroll
     for (int d = 0; d < P; ++d) {
-      const int64_t c = cb + d;
-      const bool live = c < nchunks;  // uniform
-      const int buf = (int)(c & 1);
+      const int64_t t = tb + d;
+      const bool live = t < nsteps;  // uniform over the block
+      const int buf = (int)(t & 1);
       if (live) store_a(buf, d);
       u32x4 b_cur[NB][TN];
 #pragma unroll
@@ -138,11 +151,12 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) b_cur[mat][tn] = b_reg[d][mat][tn];
       if (live) __syncthreads();
-      // refill the slot with chunk c + P (zeros past the end), then compute
-      load(c + P, d);
+      // refill the slot with step t + P (zeros past the end), then compute
+      // (a group's step past the last chunk computes on zeros)
+      load(t + P, d);
       __builtin_amdgcn_sched_barrier(0);
       if (live) {
-        const int8_t* la = &lds_a[buf][0];
+        const int8_t* la = &lds_a[buf][kg][0];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           v4i a[TM];
@@ -167,8 +181,42 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
     }
   }
 
-  // ---- epilogue
+  // K groups 1 .. KS-1 hand their partial tiles to group 0 through the
+  // (now free) activation stages
+  if constexpr (KS > 1) {
+    static_assert((KS - 1) * 4 * NB * TM * TN * 64 * 16 <= 2 * KS * BM * kLdsPitch,
+                  "partial tiles fit in the activation stages");
+    v4i* part = reinterpret_cast<v4i*>(&lds_a[0][0][0]);
+    __syncthreads();  // every group is done reading the stages
+    if (kg > 0) {
+#pragma unroll
+      for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            part[((((kg - 1) * 4 + wl) * NB + mat) * TM + tm) * TN * 64 + tn * 64 + lane] =
+                acc[mat][tm][tn];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int k = 1; k < KS; ++k)
+#pragma unroll
+        for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+              acc[mat][tm][tn] +=
+                  part[((((k - 1) * 4 + wl) * NB + mat) * TM + tm) * TN * 64 + tn * 64 + lane];
+    }
+  }
+  const bool owner = kg == 0;
+
+  // ---- epilogue (group 0)
   if constexpr (EPI == MF_STORE) {
+    if (!owner) return;
     const float sw = s0[0];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
@@ -192,38 +240,40 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(
   } else {
     __shared__ float red[WAVES_N][BM];
     const float sg = s0[0], su = s1[0];
+    if (owner) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
+      for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int lrow = 16 * (wm * TM + tm) + 4 * g + r;
-        const int64_t m = m0 + lrow;
-        float hmax = 0.0f;
-        if (m < M) {
-          const int32_t rsm = rowsum[m];
-          const float xs = x_scale[m];
-          const float scg = __fmul_rn(sg, xs), scu = __fmul_rn(su, xs);
+        for (int r = 0; r < 4; ++r) {
+          const int lrow = 16 * (wm * TM + tm) + 4 * g + r;
+          const int64_t m = m0 + lrow;
+          float hmax = 0.0f;
+          if (m < M) {
+            const int32_t rsm = rowsum[m];
+            const float xs = x_scale[m];
+            const float scg = __fmul_rn(sg, xs), scu = __fmul_rn(su, xs);
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) {
-            const int64_t n = n0 + 16 * (wn * TN + tn) + li;
-            if (n < N) {
-              const float gv = dequant_fast(acc[0][tm][tn][r] - rsm, scg);
-              const float uv = dequant_fast(acc[1][tm][tn][r] - rsm, scu);
-              const float a = gv > 0.0f ? gv : 0.0f;
-              const float h = __fmul_rn(__fmul_rn(a, a), uv);
-              Y[m * N + n] = h;
-              hmax = fmaxf(hmax, fabsf(h));
+            for (int tn = 0; tn < TN; ++tn) {
+              const int64_t n = n0 + 16 * (wn * TN + tn) + li;
+              if (n < N) {
+                const float gv = dequant_fast(acc[0][tm][tn][r] - rsm, scg);
+                const float uv = dequant_fast(acc[1][tm][tn][r] - rsm, scu);
+                const float a = gv > 0.0f ? gv : 0.0f;
+                const float h = __fmul_rn(__fmul_rn(a, a), uv);
+                Y[m * N + n] = h;
+                hmax = fmaxf(hmax, fabsf(h));
+              }
             }
           }
-        }
-        // max over the 16 lanes holding this row
+          // max over the 16 lanes holding this row
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
-        if (li == 0) red[wn][lrow] = hmax;
+          for (int o = 8; o > 0; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o));
+          if (li == 0) red[wn][lrow] = hmax;
+        }
       }
     }
     __syncthreads();
-    for (int lrow = tid; lrow < BM; lrow += 256) {
+    for (int lrow = tid; lrow < BM; lrow += NT) {
       float v = red[0][lrow];
 #pragma unroll
       for (int w = 1; w < WAVES_N; ++w) v = fmaxf(v, red[w][lrow]);
@@ -612,7 +662,7 @@ static hipError_t stream_launch(const int8_t* Xq, const float* xs, const int32_t
 #undef BL_STREAM_GO
 }
 
-template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI, int P = 1>
+template <int TM, int TN, int WAVES_M, int WAVES_N, int EPI, int P = 1, int KS = 1>
 static hipError_t mfma_launch(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                               int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
                               const float* s1, int64_t N, float* Y, int32_t* acc_out,
@@ -621,9 +671,9 @@ static hipError_t mfma_launch(const int8_t* Xq, const float* xs, const int32_t* 
   constexpr int BN = 16 * TN * WAVES_N;
   const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
   if (nparts) *nparts = (int)nbn;
-  hipLaunchKernelGGL((mfma_gemm_kernel<TM, TN, WAVES_M, WAVES_N, EPI, P>), dim3((unsigned)(nbm * nbn)),
-                     dim3(256), 0, s, Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts,
-                     (int)nbn);
+  hipLaunchKernelGGL((mfma_gemm_kernel<TM, TN, WAVES_M, WAVES_N, EPI, P, KS>),
+                     dim3((unsigned)(nbm * nbn)), dim3(256 * KS), 0, s, Xq, xs, rs, M, Kp, W0, s0, W1,
+                     s1, N, Y, acc_out, gh_parts, (int)nbn);
   return hipGetLastError();
 }
 
@@ -644,14 +694,18 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
   // 17 <= M <= 64: 32 x 32 block tiles (four 16 x 16 wave tiles) keep more
-  // blocks in flight than 64-row tiles for these weight-streaming shapes.
-  // Loads of 4 chunks in flight for long K (and at up to 32 tokens), else 2:
-  // at 64 tokens 2560 -> 6912 took 9.5 us with 2 against 10.5 with 4 and
-  // 10.2 with 1, 6912 -> 2560 13.3 us with 4 against 16.5 with 2 and 19.5
-  // with 1
-  if (M <= 32 || (Kp + kChunk - 1) / kChunk >= 16)
-    return mfma_launch<1, 1, 2, 2, MF_STORE, 4>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
-                                                acc_out, nullptr, nullptr, s);
+  // blocks in flight than 64-row tiles for these weight-streaming shapes,
+  // with 2 chunks of loads in flight per wave; long K split over 4 groups of
+  // waves in the block (6912 -> 2560 at 64 tokens: 9.9 us against 12.6 with
+  // one group and 4 chunks in flight, 19.5 with one chunk; at 32 tokens the
+  // same), shorter K over 2 groups up to 32 tokens (2560 -> 6912: 6.3 against
+  // 6.7 us) and one group above (8.3 against 8.4 us at 64 tokens)
+  if ((Kp + kChunk - 1) / kChunk >= 16)
+    return mfma_launch<1, 1, 2, 2, MF_STORE, 2, 4>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N,
+                                                   Y, acc_out, nullptr, nullptr, s);
+  if (M <= 32)
+    return mfma_launch<1, 1, 2, 2, MF_STORE, 2, 2>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N,
+                                                   Y, acc_out, nullptr, nullptr, s);
   return mfma_launch<1, 1, 2, 2, MF_STORE, 2>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                               acc_out, nullptr, nullptr, s);
 }
