@@ -238,10 +238,11 @@ int bitlinear_forward_kernel(const int8_t *Xq, const float *x_scale, const int32
 /*
  * bitlinear_forward_fused -- one BitLinear straight from float activations:
  * per-token quantisation ([P1] "BitNet b1.58" activation_quant) and the
- * product with fused dequant in one call.  For M == 1 with Kp <= 16384 this
- * is a single kernel (every block quantises the token into LDS; identical
- * bits); otherwise bitlinear_quant_act into the workspace, then
- * bitlinear_forward.  Results are bit-identical to that two-call sequence.
+ * product with fused dequant in one call.  For one token with Kp <= 7168,
+ * or Kp <= 8192 when the packed matrix has 16 MiB or more, it is a single
+ * kernel (every block quantises the token into LDS; identical bits);
+ * otherwise bitlinear_quant_act into the workspace, then bitlinear_forward.
+ * Results are bit-identical to that two-call sequence.
  *
  *  X        [M][K] float32 (BL_F32) or bfloat16 (BL_BF16), device.
  *  Wp, w_scale, N, Y   as bitlinear_forward.

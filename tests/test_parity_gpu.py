@@ -397,6 +397,11 @@ def test_rmsnorm_on_mean_squares_at_binary32_midpoints(M):
                                         (1, 8192, 300, True), (3, 700, 130, False), (80, 512, 200, True),
                                         # packed matrices of >= 16 MiB: the streaming GEMV
                                         (1, 8192, 28672, False), (1, 8192, 16400, True),
+                                        # 2..5 tokens on large layers (quantiser, then the
+                                        # streaming MFMA product), ragged K and N
+                                        (2, 8192, 28672, False), (3, 1000, 25601, True),
+                                        (4, 4096, 26000, False), (4, 8192, 25600, True),
+                                        (2, 2052, 32000, False), (5, 1024, 25600, False),
                                         (1, 5000, 13301, False), (1, 4000, 17001, True),
                                         (1, 4097, 16500, False), (1, 8192, 12001, False),
                                         (1, 4096, 40000, True)])
