@@ -22,37 +22,41 @@ __global__ void zero_bins_kernel(uint64_t* bins) {
   if (i < kBins) bins[i] = 0ull;
 }
 
-// Grid-stride over 4-weight units (a float4 load when W is 16-byte aligned,
-// two units in flight per lane).  Each lane sums exactly in a 128-bit integer
-// A (four 32-bit limbs) at a fixed scale: with window base lo, a weight of bin
-// b in [lo, lo + 64) adds m * 2^(b - lo), so A * 2^(lo - 150) is the lane's
-// sum.  lo is set from the lane's first non-zero weight (40 bins below it);
-// weights outside the window go straight into the block's LDS bins.  At the
-// end limb j of A is added to bin lo + 32 j (same value, bin form), and the
-// block adds its non-empty bins to the global ones.  Bounds: each add is below
-// 2^87 and a lane adds at most 2^13 weights (n <= 2^32), so A < 2^128; lo is
-// kept in [1, 159] so that lo + 96 is a bin.  Integer adds throughout: the
-// result does not depend on the order.
-__device__ __forceinline__ void absmean_add(float x, int& lo, uint32_t (&a)[4],
+// Each block reads one contiguous range of 4-weight units, kAbsUnits x 256
+// at a time (float4 loads when W is 16-byte aligned).  Each lane sums exactly
+// in a 96-bit integer A (three 32-bit limbs) at a fixed scale: with window
+// base lo, a weight of bin b in [lo, lo + kAbsWin) adds m * 2^(b - lo) < 2^63,
+// so A * 2^(lo - 150) is the lane's sum.  lo is set from the largest finite
+// bin among the lane's first loads holding a non-zero weight (kAbsBelow bins
+// below it, so the window reaches 2^9 above that weight); subnormal weights
+// and weights outside the window go straight into the block's LDS bins
+// (zeros, Inf and NaN add nothing).  At the end limb j of A is added to bin
+// lo + 32 j (same value, bin form), and the block adds its non-empty bins to
+// the global ones.  Bounds: a lane adds at most 2^13 + 16 weights (n <= 2^32
+// over 2^19 lanes, ranges rounded up to 1024 units), so A < 2^77; lo is kept
+// in [1, 190] so that lo + 64 is a bin.  Integer adds throughout: the result
+// does not depend on the order.
+constexpr int kAbsWin = 40;
+constexpr int kAbsBelow = 30;
+constexpr int kAbsUnits = 4;
+
+__device__ __forceinline__ void absmean_add(uint32_t bits, int lo, uint32_t (&a)[3],
                                             unsigned long long* lbins) {
-  int b;
-  uint32_t m;
-  bin_of(x, b, m);
-  if (lo == 0 && m != 0u) lo = min(max(b - 40, 1), 159);
-  const int sh = b - lo;
-  if ((unsigned)sh < 64u || m == 0u) {
-    const uint64_t p = (uint64_t)m << (sh & 31);
-    const uint32_t p0 = (uint32_t)p, p1 = (uint32_t)(p >> 32);
-    const bool hi = sh >= 32;
-    uint64_t t = (uint64_t)a[0] + (hi ? 0u : p0);
-    a[0] = (uint32_t)t;
-    t = (uint64_t)a[1] + (hi ? p0 : p1) + (t >> 32);
-    a[1] = (uint32_t)t;
-    t = (uint64_t)a[2] + (hi ? p1 : 0u) + (t >> 32);
-    a[2] = (uint32_t)t;
-    a[3] += (uint32_t)(t >> 32);
-  } else {
-    atomicAdd(&lbins[b], (unsigned long long)m);
+  // in the window e >= lo >= 1 and e < lo + kAbsWin <= 229: a normal finite
+  // weight, m = mantissa with its implicit bit
+  const int sh = (int)((bits >> 23) & 0xffu) - lo;
+  if ((unsigned)sh < (unsigned)kAbsWin) {
+    const uint64_t p = (uint64_t)((bits & 0x7fffffu) | 0x800000u) << sh;
+    uint32_t c;
+    a[0] = __builtin_addc(a[0], (uint32_t)p, 0u, &c);
+    a[1] = __builtin_addc(a[1], (uint32_t)(p >> 32), c, &c);
+    a[2] += c;
+  } else if (bits & 0x7fffffffu) {
+    // outside the window, subnormal, Inf or NaN (the last two add nothing)
+    int b;
+    uint32_t mb;
+    bin_of(__uint_as_float(bits), b, mb);
+    if (mb) atomicAdd(&lbins[b], (unsigned long long)mb);
   }
 }
 
@@ -62,31 +66,47 @@ __global__ __launch_bounds__(256) void absmean_bins_kernel(const float* __restri
   const int tid = threadIdx.x;
   for (int i = tid; i < kBins; i += 256) lbins[i] = 0ull;
   __syncthreads();
+  // block b reads units [b * per, (b + 1) * per), 16 KiB contiguous per step
   const int64_t units = (n + 3) / 4;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t per = ((units + gridDim.x - 1) / gridDim.x + 1023) / 1024 * 1024;
+  const int64_t ub = (int64_t)blockIdx.x * per;
+  const int64_t ue = ub + per < units ? ub + per : units;
   int lo = 0;
-  uint32_t a[4] = {0u, 0u, 0u, 0u};
-  for (int64_t u0 = (int64_t)blockIdx.x * 256 + tid; u0 < units; u0 += 2 * stride) {
-    float x[2][4];
+  uint32_t a[3] = {0u, 0u, 0u};
+  for (int64_t u0 = ub + tid; u0 < ue; u0 += kAbsUnits * 256) {
+    uint32_t x[kAbsUnits][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t u = u0 + h * stride;
-      if (vec && 4 * u + 3 < n) {
-        const float4 f = reinterpret_cast<const float4*>(W)[u];
+    for (int h = 0; h < kAbsUnits; ++h) {
+      const int64_t u = u0 + h * 256;
+      if (vec && u < ue && 4 * u + 3 < n) {
+        const uint4 f = reinterpret_cast<const uint4*>(W)[u];
         x[h][0] = f.x; x[h][1] = f.y; x[h][2] = f.z; x[h][3] = f.w;
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[h][i] = 4 * u + i < n ? W[4 * u + i] : 0.0f;
+        for (int i = 0; i < 4; ++i)
+          x[h][i] = u < ue && 4 * u + i < n ? __float_as_uint(W[4 * u + i]) : 0u;
       }
     }
+    if (lo == 0) {
+      // the window: from the largest finite non-zero bin of these loads
+      int bm = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < kAbsUnits; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u = x[h][i] & 0x7fffffffu;
+          if (u != 0u && u < 0x7f800000u) bm = max(bm, max((int)(u >> 23), 1));
+        }
+      if (bm) lo = min(max(bm - kAbsBelow, 1), 190);
+    }
+#pragma unroll
+    for (int h = 0; h < kAbsUnits; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) absmean_add(x[h][i], lo, a, lbins);
   }
   if (lo != 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 3; ++j)
       if (a[j]) atomicAdd(&lbins[lo + 32 * j], (unsigned long long)a[j]);
   }
   __syncthreads();
@@ -128,6 +148,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
   const float* row = W + (int64_t)n * K;
   uint32_t* out = Wp + (int64_t)n * (upr / L);
   const float d = MODE == 0 ? __fadd_rn(w_scale[0], kEps) : 1.0f;
+  // d >= 1e-5: d / 2 is exact; non-finite scales and weights take the division
+  const bool dfin = __builtin_isfinite(d);
+  const float hd = __fmul_rn(d, 0.5f);
   float w[U][4];
 #pragma unroll
   for (int i = 0; i < U; ++i) {
@@ -155,6 +178,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ W, 
         if (in) {
           if constexpr (MODE == 1) {
             code = w[i][b] >= 0.0f ? 2u : 0u;
+          } else if (dfin && __builtin_isfinite(w[i][b])) {
+            // rne(fl(w / d)) is non-zero exactly when |w| > d / 2: at or
+            // below it the quotient is at most 1/2 and rounds to 0; the next
+            // float above d / 2 = m 2^(e-1) (1 <= m < 2) is d / 2 + 2^(e-24),
+            // whose quotient exceeds 1/2 + 2^-25 and so rounds above 1/2
+            code = fabsf(w[i][b]) > hd ? (w[i][b] > 0.0f ? 2u : 0u) : 1u;
           } else {
             float q = __builtin_rintf(__fdiv_rn(w[i][b], d));
             q = fminf(fmaxf(q, -1.0f), 1.0f);

@@ -175,6 +175,39 @@ def test_weight_scale_wide_dynamic_range():
         assert host(sc)[0].view(np.uint32) == np.float32(g).view(np.uint32)
 
 
+def test_ternary_codes_at_the_rounding_threshold():
+    """Weights a few ulps either side of d/2 (d = scale + 1e-5, both signs,
+    d/2 itself included): the code is non-zero exactly when the correctly
+    rounded quotient w / d exceeds 1/2, i.e. above d/2 and not at it.  The
+    placed weights barely move the scale; they are re-placed until the scale
+    is a fixed point."""
+    rng = np.random.default_rng(43)
+    for scale in (1.0, 1.37, 1.93, 3.1e-3):
+        W = (rng.standard_normal((48, 640)) * scale).astype(np.float32)
+        idx = rng.choice(W.size, 64, replace=False)
+        g = oracle.weight_scale(W)
+        for _ in range(20):
+            d = np.float32(g) + oracle.EPS
+            half = d * np.float32(0.5)
+            vals, v = [], half
+            for _k in range(4):
+                v = np.nextafter(v, np.float32(0), dtype=np.float32)
+            for _k in range(9):
+                vals += [v, -v]
+                v = np.nextafter(v, np.float32(np.inf), dtype=np.float32)
+            Wn = W.copy()
+            Wn.flat[idx[:len(vals)]] = np.asarray(vals, np.float32)
+            g2 = oracle.weight_scale(Wn)
+            if np.float32(g2) == np.float32(g):
+                break
+            g = g2
+        else:
+            raise AssertionError("the scale did not settle")
+        t = oracle.ternarize(np.asarray(vals, np.float32), np.float32(g))
+        assert (t == 0).sum() == 10 and (t != 0).sum() == 8  # the threshold is crossed
+        check_pack(Wn, "ternary")
+
+
 def test_quant_edge_rows_and_bf16():
     X = synth.normal(22, 1, (6, 700))
     X[1] = 0.0
