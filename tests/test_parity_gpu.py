@@ -127,6 +127,10 @@ def test_single_layer_512_to_400_all_kernels():
     # one token, packed matrix >= 16 MiB (the streaming GEMV), ragged K and odd N
     (1, 5000, 13301), (1, 4000, 17001), (1, 8192, 16385), (1, 8192, 8192), (1, 8192, 12001),
     (1, 4096, 40000),
+    # the largest K, N and M the boundary accepts (65536 each), one at a time
+    (1, 65536, 200), (8, 65536, 100), (40, 65536, 48), (100, 65536, 64),
+    (1, 100, 65536), (8, 100, 65536), (40, 200, 65536), (100, 100, 65536),
+    (65536, 100, 40),
 ])
 def test_random_ragged_shapes(M, K, N):
     d = synth.random_case(1000 + M * 7 + N, M, K, N)
@@ -355,7 +359,10 @@ def test_ffn_2b_subln(M):
                                          (17, 512, 1000, False), (40, 1000, 3000, False),
                                          (100, 256, 520, False), (256, 512, 1024, False),
                                          (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
-                                         (100, 256, 520, True)])
+                                         (100, 256, 520, True),
+                                         # the largest D and F
+                                         (1, 65536, 64, False), (3, 65536, 48, True),
+                                         (1, 64, 65536, False), (2, 100, 65536, True)])
 def test_ffn_ragged_shapes(M, D, F, subln):
     s = 500 + M
     x = synth.normal(s, 1, (M, D))
@@ -435,6 +442,9 @@ def test_rmsnorm_on_mean_squares_at_binary32_midpoints(M):
                                         (2, 8192, 28672, False), (3, 1000, 25601, True),
                                         (4, 4096, 26000, False), (4, 8192, 25600, True),
                                         (2, 2052, 32000, False), (5, 1024, 25600, False),
+                                        # the largest K and N
+                                        (1, 65536, 100, False), (2, 65536, 40, True),
+                                        (1, 100, 65536, True),
                                         (1, 5000, 13301, False), (1, 4000, 17001, True),
                                         (1, 4097, 16500, False), (1, 8192, 12001, False),
                                         (1, 4096, 40000, True)])
@@ -491,6 +501,7 @@ def check_forward1(q, gx, t, gw, Xq, xs, xr, Wb, ws):
     (1, 8320, 70), (1, 24640, 20), (1, 40000, 9), (2, 64, 16), (5, 129, 64), (8, 1040, 257),
     (16, 512, 400), (16, 8192, 70), (17, 63, 15), (33, 1000, 100), (64, 2560, 96),
     (65, 300, 130), (100, 1040, 257), (130, 128, 70),
+    (1, 65536, 100), (8, 100, 65536), (100, 65536, 40),
 ])
 def test_binary_1bit_ragged_shapes(M, K, N):
     d = synth.random_case(4000 + M * 7 + N, M, K, N)
@@ -581,7 +592,7 @@ def check_a48(X, n_out, t, g, Wp, sc, bf16=False):
     (1, 100, 40, 0, False), (1, 100, 40, 100, False), (1, 100, 40, 1000, False),
     (1, 16448, 33, 165, False), (3, 700, 130, 7, False), (16, 512, 400, 5, False),
     (64, 2560, 96, 26, True), (100, 1040, 257, 10, False), (1, 40000, 9, 400, False),
-    (2, 20000, 17, 200, False),
+    (2, 20000, 17, 200, False), (1, 65536, 40, 655, False), (3, 65536, 24, 100, True),
 ])
 def test_a48_quant_and_forward(M, K, N, n_out, bf16):
     d = synth.random_case(5000 + K + N + M, M, K, N)
