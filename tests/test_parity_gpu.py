@@ -139,6 +139,30 @@ def test_random_ragged_shapes(M, K, N):
     check_forward(q, gx, t, g, Xq, xs, xr, Wp, sc, kernels_for(M))
 
 
+def test_outputs_past_two_to_the_31_elements():
+    """M = N = 65536 (K = 64): 2^32 outputs, so rows from 32768 on start past
+    element 2^31 and byte offset 8 GiB.  Sampled rows (first, last, both sides
+    of the 2^31 boundary and random ones) against the oracle, for the 2-bit
+    and the 1-bit layouts."""
+    M, K, N = 65536, 64, 65536
+    d = synth.random_case(77, M, K, N)
+    g, t, Wp, sc = check_pack(d["W"])
+    q, gx, rs, Xq, xs, xr = check_quant(d["X"])
+    rng = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([[0, 1, 32767, 32768, 32769, M - 1],
+                                     rng.integers(0, M, 40)]))
+    ref = oracle.dequant(oracle.int_linear(q[rows], t), gx[rows], g)
+    ridx = torch.from_numpy(rows).to(DEV)
+    Y = B.bitlinear_forward(Xq, xs, xr, K, Wp, sc, N)
+    assert_rel(host(Y.index_select(0, ridx)), ref)
+    g1, t1, Wb, sc1 = check_pack1(d["W"])
+    ref1 = oracle.dequant(oracle.int_linear(q[rows], t1), gx[rows], g1)
+    B.bitlinear_forward_1bit(Xq, xs, xr, K, Wb, sc1, N, out=Y)
+    assert_rel(host(Y.index_select(0, ridx)), ref1)
+    del Y
+    torch.cuda.empty_cache()
+
+
 def test_binary_mode_and_degenerate_weights():
     rng = np.random.default_rng(21)
     W = rng.standard_normal((70, 200)).astype(np.float32)
