@@ -77,6 +77,8 @@ def test_quant_validation():
     lib = B.lib()
     assert lib.bitlinear_quant_act(None, 0, 1, 8, FAKE, FAKE, FAKE, None) == B.BL_EINVAL
     assert lib.bitlinear_quant_act(FAKE, 2, 1, 8, FAKE, FAKE, FAKE, None) == B.BL_EINVAL
+    # the row sums are required output (the forward takes them as input)
+    assert lib.bitlinear_quant_act(FAKE, 0, 1, 8, FAKE, FAKE, None, None) == B.BL_EINVAL
     assert lib.bitlinear_quant_act(FAKE, 0, 0, 8, FAKE, FAKE, FAKE, None) == B.BL_ESHAPE
     assert lib.bitlinear_quant_act(FAKE, 0, 1, -1, FAKE, FAKE, FAKE, None) == B.BL_ESHAPE
     assert lib.bitlinear_quant_act(FAKE, 0, 1, 8, ODD, FAKE, FAKE, None) == B.BL_EALIGN
