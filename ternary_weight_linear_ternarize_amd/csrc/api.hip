@@ -318,7 +318,11 @@ static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
   }
   if (e != hipSuccess) return BL_EHIP;
   if (subln_w) {
-    // SubLN: RMSNorm of h, then its int8 codes
+    // SubLN: RMSNorm of h, then its int8 codes; one token: both inside the
+    // down GEMV
+    if (M == 1 && bl::gemv_norm_ok(F))
+      return hip_status(
+          bl::launch_gemv_norm(h, F, subln_w, subln_eps, Wd, sd, D, Y, hn, qh, gh, rsh, s));
     e = bl::launch_rmsnorm_quant(h, false, M, F, subln_w, subln_eps, hn, qh, gh, rsh, s);
   } else if (M == 1 && bl::gemv_fused_ok(F, 0)) {
     // requantise h inside the down GEMV (scale from the partial maxima)

@@ -73,6 +73,16 @@ hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, in
                              const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
                              int8_t* xq_out, float* xs_out, int32_t* rs_out, hipStream_t s);
 
+// One token of a float32 row RMS-normalised (norm_w, eps; the exact mean
+// square), quantised and multiplied in one kernel (every block redoes the
+// norm; block 0 writes xn, the codes, the scale and the row sum): the SubLN
+// block's down projection.  Needs gemv_norm_ok(K) (padded K <= 8192).
+bool gemv_norm_ok(int64_t K);
+hipError_t launch_gemv_norm(const float* X, int64_t K, const float* norm_w, float eps,
+                            const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                            float* xn_out, int8_t* xq_out, float* xs_out, int32_t* rs_out,
+                            hipStream_t s);
+
 // Y = dequant(Xq . T^T) on MFMA: skinny (M <= 64, tiled == false) or the
 // 128 x 128 tiled kernel.
 hipError_t launch_mfma(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,

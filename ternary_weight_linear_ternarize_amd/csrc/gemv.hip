@@ -642,10 +642,19 @@ static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s, int* nblocks = nullpt
   hipLaunchKernelGGL((gemv_kernel<KCV, R, EPI, XSRC, NT>), dim3(blocks), dim3(NT), 0, s, a)
   if constexpr (XSRC == XS_NF32 || XSRC == XS_NBF16) {
     // the normalising prologue holds the row in registers: one chunk per lane
-    // (92 VGPRs; two chunks take 171)
-    if (C > 64) return hipErrorInvalidValue;
-    BL_GEMV_CASE(1);
-    return hipGetLastError();
+    // for the gate/up form (92 VGPRs; two chunks take 171), up to two for the
+    // plain product
+    if (C <= 64) {
+      BL_GEMV_CASE(1);
+      return hipGetLastError();
+    }
+    if constexpr (EPI == EPI_STORE) {
+      if (C <= 128) {
+        BL_GEMV_CASE(2);
+        return hipGetLastError();
+      }
+    }
+    return hipErrorInvalidValue;
   }
   if (C <= 64) BL_GEMV_CASE(1);
   else if (C <= 128) BL_GEMV_CASE(2);
@@ -722,6 +731,24 @@ hipError_t launch_gemv_parts(const float* X, const float* gparts, int nparts, in
   a.rs_out = rs_out;
   if ((N + 31) / 32 >= kWideGemvBlocks) return gemv_dispatch<4, EPI_STORE, XS_PARTS, 512>(a, s);
   return gemv_dispatch<2, EPI_STORE, XS_PARTS, 512>(a, s);
+}
+
+bool gemv_norm_ok(int64_t K) { return (K + 63) / 64 <= 128; }
+
+hipError_t launch_gemv_norm(const float* X, int64_t K, const float* norm_w, float eps,
+                            const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                            float* xn_out, int8_t* xq_out, float* xs_out, int32_t* rs_out,
+                            hipStream_t s) {
+  GemvArgs a = base_args(K, Wp, ws, N, Y);
+  a.x = X;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.xn_out = xn_out;
+  a.xq_out = xq_out;
+  a.xs_out = xs_out;
+  a.rs_out = rs_out;
+  if ((N + 31) / 32 >= kWideGemvBlocks) return gemv_dispatch<4, EPI_STORE, XS_NF32, 512>(a, s);
+  return gemv_dispatch<2, EPI_STORE, XS_NF32, 512>(a, s);
 }
 
 constexpr int kGateupR = 4;  // weight rows per wave in the gate/up GEMV (half gate, half up)
