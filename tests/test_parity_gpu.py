@@ -384,6 +384,10 @@ def test_ffn_2b_subln(M):
                                          (100, 256, 520, False), (256, 512, 1024, False),
                                          (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
                                          (100, 256, 520, True),
+                                         # SubLN inside the one-token down GEMV: two chunks
+                                         # per lane with 2 and 4 rows per wave, F at its limit
+                                         (1, 8000, 7000, True), (1, 700, 8192, True),
+                                         (1, 700, 8193, True),
                                          # the largest D and F
                                          (1, 65536, 64, False), (3, 65536, 48, True),
                                          (1, 64, 65536, False), (2, 100, 65536, True)])
