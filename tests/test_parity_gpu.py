@@ -249,6 +249,41 @@ def test_quant_edge_rows_and_bf16():
     check_quant(x)
 
 
+def test_nonfinite_rows_leave_the_other_rows_exact():
+    """NaN and Inf inputs give unspecified results, but every call completes
+    and the tokens whose rows are finite come out bit for bit as the oracle
+    computes them without the others (quantisation, RMSNorm and the products
+    are per token), through the 8- and 40-token products and the FFN block."""
+    for M, K, N in ((8, 1000, 300), (40, 700, 200)):
+        d = synth.random_case(900 + M, M, K, N)
+        X = d["X"].copy()
+        bad = [1, 5]
+        X[1, 7] = np.nan
+        X[5, :3] = [np.inf, -np.inf, np.nan]
+        good = np.array([m for m in range(M) if m not in bad])
+        g, t, Wp, sc = check_pack(d["W"])
+        Xq, xs, xr = B.bitlinear_quant_act(to_dev(X))
+        for kern in kernels_for(M):
+            Y, A = B.bitlinear_forward(Xq, xs, xr, K, Wp, sc, N, with_acc=True, kernel=kern)
+            q, gx, rs = oracle.act_quant(X[good])
+            acc = oracle.int_linear(q, t)
+            np.testing.assert_array_equal(host(A)[good], acc)
+            assert_rel(host(Y)[good], oracle.dequant(acc, gx, g))
+    M, D, F = 8, 256, 520
+    x = synth.normal(950, 1, (M, D))
+    x[2, 10] = np.nan
+    x[6, 0] = np.inf
+    good = np.array([0, 1, 3, 4, 5, 7])
+    ws = [synth.normal(950, 2 + i, shp, 0.02) for i, shp in enumerate(((F, D), (F, D), (D, F)))]
+    q = [oracle.quantize_weights(w) for w in ws]
+    pk = [B.bitlinear_pack(to_dev(w)) for w in ws]
+    eps = 1e-6
+    ref = oracle.ffn(x[good], None, eps, q[0][1], q[0][0], q[1][1], q[1][0], q[2][1], q[2][0])
+    Y, _ = B.bitnet_ffn_forward(to_dev(x), None, eps, pk[0][0], pk[0][1], pk[1][0], pk[1][1],
+                                pk[2][0], pk[2][1], D, F)
+    assert_rel(host(Y)[good], ref["y"])
+
+
 def test_decode_2b_gemv_up_and_down_full():
     d = synth.decode_2b()
     for Wn, xn in (("W_up", "x"), ("W_down", "x_d")):
