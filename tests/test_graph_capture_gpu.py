@@ -62,7 +62,7 @@ def check_replays(call, outputs, scratch, checked):
             same_bits(a, b)
 
 
-@pytest.mark.parametrize("M,subln", [(1, False), (8, False), (64, False), (8, True)])
+@pytest.mark.parametrize("M,subln", [(1, False), (8, False), (64, False), (1, True), (8, True)])
 def test_graph_ffn(M, subln):
     f = synth.ffn_2b()
     D, F = synth.FFN_2B["D"], synth.FFN_2B["F"]
