@@ -3,8 +3,9 @@
 The compute lives in ``libbitlinear.so`` (hand-written HIP kernels for gfx950
 behind the C ABI declared in ``include/bitlinear.h``).  ``binding`` is a thin
 ctypes layer over that ABI (it loads the library on first use and raises if
-it was not built); ``synth`` draws the seeded synthetic inputs.
+it was not built); ``layers`` holds BitLinear and BitNetFFN objects over it;
+``synth`` draws the seeded synthetic inputs.
 """
-from . import binding, synth  # noqa: F401
+from . import binding, layers, synth  # noqa: F401
 
-__all__ = ["binding", "synth"]
+__all__ = ["binding", "layers", "synth"]
