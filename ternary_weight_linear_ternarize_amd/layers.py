@@ -26,13 +26,18 @@ class BitLinear:
     (sign weights in the 2-bit layout) or B.BL_BINARY_1BIT (sign weights, one
     bit each).  x [..., K] float32 or bfloat16 -> y [..., N] float32: the
     per-token int8 quantisation, the ternary product and the dequantisation
-    (one fused call for the 2-bit layouts)."""
+    (one fused call for the 2-bit layouts).  a48_outliers = n (2-bit layouts
+    only) takes the BitNet a4.8 activations instead (youngju.dev "BitNet
+    a4.8"): per token the n largest |x| in 8 bits, the rest in 4 bits."""
 
-    def __init__(self, weight, mode=B.BL_TERNARY):
+    def __init__(self, weight, mode=B.BL_TERNARY, a48_outliers=None):
         if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
             raise ValueError("weight must be a 2-D tensor [out_features, in_features]")
         self.out_features, self.in_features = (int(d) for d in weight.shape)
         self.mode = mode
+        if a48_outliers is not None and mode == B.BL_BINARY_1BIT:
+            raise ValueError("a4.8 activations run on the 2-bit layouts")
+        self.a48_outliers = a48_outliers
         self.weight_packed, self.weight_scale = B.bitlinear_pack(weight.contiguous(), mode)
         self._ws = {}
 
@@ -45,7 +50,10 @@ class BitLinear:
     def __call__(self, x):
         X = _tokens(x, self.in_features, "x")
         N, K = self.out_features, self.in_features
-        if self.mode == B.BL_BINARY_1BIT:
+        if self.a48_outliers is not None:
+            q = B.bitlinear_quant_act_a48(X, self.a48_outliers)
+            Y, _ = B.bitlinear_forward_a48(q, K, self.weight_packed, self.weight_scale, N)
+        elif self.mode == B.BL_BINARY_1BIT:
             Xq, xs, xr = B.bitlinear_quant_act(X)
             Y = B.bitlinear_forward_1bit(Xq, xs, xr, K, self.weight_packed, self.weight_scale, N)
         else:

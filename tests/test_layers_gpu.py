@@ -57,6 +57,19 @@ def test_bitlinear_layer_matches_oracle(mode):
         layer(_dev(X[..., :500]))
 
 
+def test_bitlinear_layer_a48_matches_oracle():
+    W = synth.normal(73, 1, (300, 700))
+    X = synth.normal(73, 2, (2, 5, 700))
+    layer = layers.BitLinear(_dev(W), a48_outliers=7)
+    Y = layer(_dev(X))
+    assert tuple(Y.shape) == (2, 5, 300)
+    g, t, _ = oracle.quantize_weights(W, "ternary")
+    ref = oracle.bitlinear_a48(X.reshape(-1, 700), t, g, 7)["y"]
+    assert _rel(_host(Y).reshape(-1, 300), ref) <= 1e-5
+    with pytest.raises(ValueError):
+        layers.BitLinear(_dev(W), B.BL_BINARY_1BIT, a48_outliers=7)
+
+
 @pytest.mark.parametrize("subln", [False, True])
 def test_ffn_layer_matches_oracle(subln):
     D, F = 256, 600
