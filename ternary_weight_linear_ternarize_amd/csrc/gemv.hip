@@ -214,6 +214,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
   constexpr int NXI = (256 * KC + NT - 1) / NT;  // int8: 16-byte pieces per thread
   int4 xi[NXI];
   float xv[NWT][4];
+  float nwv[NORM ? NWT : 1][4];  // NORM: the norm weights of this thread's words
   float g = 0.0f;
   uint32_t gp[kGpPerThread] = {};  // XS_PARTS: partial maxima (float bits)
   if constexpr (!FUSED) {
@@ -258,6 +259,18 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
         }
       }
     }
+    if constexpr (NORM) {
+      // the norm weights ride with the row (branch-free buffer loads; past
+      // K, or with no weights, they read 0) instead of being fetched after
+      // the mean square
+      const buf_rsrc rw = make_buf_rsrc(a.norm_w, a.norm_w ? (uint32_t)(4 * K) : 0u);
+#pragma unroll
+      for (int j = 0; j < NWT; ++j)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          nwv[j][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rw, (uint32_t)(4 * (4 * (tid + NT * j) + b)), 0, 0));
+    }
   }
 
   uint4 w[R][KC];
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
           const int k = 4 * wd + b;
           const bool in = wd < nw && k < K;
           float v = __fmul_rn(xv[j][b], r);
-          if (a.norm_w) v = __fmul_rn(v, in ? a.norm_w[k] : 0.0f);
+          if (a.norm_w) v = __fmul_rn(v, nwv[j][b]);
           xv[j][b] = in ? v : 0.0f;
           if (in && blockIdx.x == 0 && a.xn_out) a.xn_out[k] = v;
         }
@@ -655,13 +668,14 @@ static hipError_t gemv_dispatch(GemvArgs a, hipStream_t s, int* nblocks = nullpt
       }
     }
     return hipErrorInvalidValue;
+  } else {
+    if (C <= 64) BL_GEMV_CASE(1);
+    else if (C <= 128) BL_GEMV_CASE(2);
+    else if (C <= 192) BL_GEMV_CASE(3);
+    else BL_GEMV_CASE(4);
+    return hipGetLastError();
   }
-  if (C <= 64) BL_GEMV_CASE(1);
-  else if (C <= 128) BL_GEMV_CASE(2);
-  else if (C <= 192) BL_GEMV_CASE(3);
-  else BL_GEMV_CASE(4);
 #undef BL_GEMV_CASE
-  return hipGetLastError();
 }
 
 static GemvArgs base_args(int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y) {
