@@ -148,6 +148,8 @@ __global__ __launch_bounds__(64 * kB1Wpb) void mfma1_kernel(
   int8_t* xbuf0 = lds;
   int8_t* xbuf1 = lds + b1_xbuf_bytes(TMS);
   int8_t* lds_w = lds + 2 * b1_xbuf_bytes(TMS) + wave * 16 * kB1Bp;
+  TokenOperands<TMS> tok;  // the epilogue's scales and row sums, the oldest loads
+  tok.load(x_scale, rowsum, M, 0);
   const int64_t wpr = Kb / 32;
   const int C = (int)(Kb / 128);  // 16-byte pieces per weight row
   const int nseg = (int)((Kb + kB1Seg - 1) / kB1Seg);
@@ -227,8 +229,8 @@ __global__ __launch_bounds__(64 * kB1Wpb) void mfma1_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * tm + 4 * g + r;
       if (m < M && n < N) {
-        const int a = acc[tm][0][r] + acc[tm][1][r] - rowsum[m];
-        Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
+        const int a = acc[tm][0][r] + acc[tm][1][r] - tok.rs[tm][r];
+        Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, tok.xs[tm][r]));
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
     }

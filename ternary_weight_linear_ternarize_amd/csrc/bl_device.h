@@ -38,6 +38,34 @@ __device__ __forceinline__ buf_rsrc make_buf_rsrc(const void* base, uint32_t nby
                                            0x00020000);
 }
 
+// The per-token operands of an MFMA epilogue: x_scale and rowsum of the
+// tokens a lane's result registers hold (token mbase + 16 tm + 4 (lane / 16)
+// + r of 16-row tile tm, register r).  Loaded at a kernel's start as
+// branch-free buffer loads (tokens past M read 0), so their round trip
+// passes while the main loop runs instead of after it (as per-register loads
+// in the epilogue, each behind its own bounds check, they were issued and
+// waited for one at a time).
+template <int TM>
+struct TokenOperands {
+  float xs[TM][4];
+  int rs[TM][4];
+  __device__ __forceinline__ void load(const float* x_scale, const int32_t* rowsum, int64_t M,
+                                      int64_t mbase) {
+    const buf_rsrc rx = make_buf_rsrc(x_scale, (uint32_t)(4 * M));
+    const buf_rsrc rr = make_buf_rsrc(rowsum, (uint32_t)(4 * M));
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mbase + 16 * tm + 4 * g + r;
+        const uint32_t off = m < M ? (uint32_t)(4 * m) : 0x80000000u;
+        xs[tm][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+        rs[tm][r] = (int)__builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 0);
+      }
+  }
+};
+
 // s_waitcnt operand that waits until at most n (< 64) vector memory
 // operations of this wave are outstanding and leaves the other counters
 // alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt

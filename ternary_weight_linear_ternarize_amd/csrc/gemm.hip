@@ -77,6 +77,9 @@ __global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
   const int64_t nchunks = (Kp + kChunk - 1) / kChunk;
   const int64_t nsteps = (nchunks + KS - 1) / KS;    // chunks per K group (upper bound)
 
+  TokenOperands<TM> tok;  // the epilogue's scales and row sums
+  tok.load(x_scale, rowsum, M, m0 + 16 * wm * TM);
+
   // ---- loaders: P chunks of loads in flight, in registers.  Buffer loads
   // issued without branches: rows past M, words past a row's end and chunks
   // past K read as zero (zero codes, zero activations), so the compiler
@@ -224,8 +227,8 @@ __global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + 16 * (wm * TM + tm) + 4 * g + r;
         if (m >= M) continue;
-        const int32_t rsm = rowsum[m];
-        const float sc = __fmul_rn(sw, x_scale[m]);
+        const int32_t rsm = tok.rs[tm][r];
+        const float sc = __fmul_rn(sw, tok.xs[tm][r]);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int64_t n = n0 + 16 * (wn * TN + tn) + li;
@@ -249,8 +252,8 @@ __global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
           const int64_t m = m0 + lrow;
           float hmax = 0.0f;
           if (m < M) {
-            const int32_t rsm = rowsum[m];
-            const float xs = x_scale[m];
+            const int32_t rsm = tok.rs[tm][r];
+            const float xs = tok.xs[tm][r];
             const float scg = __fmul_rn(sg, xs), scu = __fmul_rn(su, xs);
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
@@ -382,6 +385,22 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // the epilogue's per-token scales and row sums first (the oldest loads:
+  // the wait for the activations below covers them); MF_A48 also the int8
+  // rows' scales
+  TokenOperands<1> tok;
+  tok.load(x_scale, rowsum, M, 0);
+  float xs8[4] = {};
+  if constexpr (EPI == MF_A48) {
+    const buf_rsrc rx = make_buf_rsrc(x_scale, (uint32_t)(4 * M));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * g + r;
+      xs8[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rx, m < M / 2 ? (uint32_t)(4 * (m + M / 2)) : 0x80000000u, 0, 0));
+    }
+  }
+
   // activations -> LDS, every load in flight at once; then the first D steps
   // of weights, so that waiting for the activations (the older loads) leaves
   // the weight steps in flight and the loop starts in the state it repeats
@@ -498,8 +517,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
       if (owner && m < M && n < N) {
-        const int a = acc[0][0][r] - rowsum[m];
-        if (Y) Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
+        const int a = acc[0][0][r] - tok.rs[0][r];
+        if (Y) Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, tok.xs[0][r]));
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
     }
@@ -513,7 +532,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
-      av[r] = m < M ? acc[0][0][r] - rowsum[m] : 0;
+      av[r] = m < M ? acc[0][0][r] - tok.rs[0][r] : 0;
       if (owner && m < M && n < N && acc_out) acc_out[(int64_t)m * N + n] = av[r];
     }
     int* ex = reinterpret_cast<int*>(lds_w);
@@ -525,8 +544,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
       if (owner && m < Mh && n < N)
-        Y[(int64_t)m * N + n] = a48_dequant(av[r], __fmul_rn(sw, x_scale[m]),
-                                            ex[(m + Mh) * 16 + li], __fmul_rn(sw, x_scale[m + Mh]));
+        Y[(int64_t)m * N + n] = a48_dequant(av[r], __fmul_rn(sw, tok.xs[0][r]),
+                                            ex[(m + Mh) * 16 + li], __fmul_rn(sw, xs8[r]));
     }
   } else {
     const float sg = s0[0], su = s1[0];
@@ -535,8 +554,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
       const int m = 4 * g + r;
       float hm = 0.0f;
       if (owner && m < M && n < N) {
-        const int32_t rsm = rowsum[m];
-        const float xs = x_scale[m];
+        const int32_t rsm = tok.rs[0][r];
+        const float xs = tok.xs[0][r];
         const float gv = dequant_fast(acc[0][0][r] - rsm, __fmul_rn(sg, xs));
         const float uv = dequant_fast(acc[1][0][r] - rsm, __fmul_rn(su, xs));
         const float t = gv > 0.0f ? gv : 0.0f;

@@ -57,6 +57,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
   // (buffer loads: the compiler keeps them where they are written, ahead of
   // the weight loads, so the staging below waits only for them; a plain load
   // sunk to its store after the weight loads would wait for everything)
+  TokenOperands<1> tok;  // the epilogue's scales and row sums, before everything else
+  tok.load(x_scale, rowsum, M, 0);
   const buf_rsrc rx = make_buf_rsrc(Xq, (uint32_t)(M * Kp));
   u32x4 xr[XR];
 #pragma unroll
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
       if (owner && m < M && n < N) {
-        const int a = acc[0][0][r] - rowsum[m];
-        if (Y) Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, x_scale[m]));
+        const int a = acc[0][0][r] - tok.rs[0][r];
+        if (Y) Y[(int64_t)m * N + n] = dequant_fast(a, __fmul_rn(sw, tok.xs[0][r]));
         if (acc_out) acc_out[(int64_t)m * N + n] = a;
       }
     }
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
       const int m = 4 * g + r;
       float hm = 0.0f;
       if (owner && m < M && n < N) {
-        const int32_t rsm = rowsum[m];
-        const float xs = x_scale[m];
+        const int32_t rsm = tok.rs[0][r];
+        const float xs = tok.xs[0][r];
         const float gv = dequant_fast(acc[0][0][r] - rsm, __fmul_rn(sg, xs));
         const float uv = dequant_fast(acc[NB - 1][0][r] - rsm, __fmul_rn(su, xs));
         const float t = gv > 0.0f ? gv : 0.0f;
