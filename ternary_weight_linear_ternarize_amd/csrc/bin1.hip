@@ -150,6 +150,7 @@ __global__ __launch_bounds__(64 * kB1Wpb) void mfma1_kernel(
   int8_t* lds_w = lds + 2 * b1_xbuf_bytes(TMS) + wave * 16 * kB1Bp;
   TokenOperands<TMS> tok;  // the epilogue's scales and row sums, the oldest loads
   tok.load(x_scale, rowsum, M, 0);
+  const float sw = w_scale[0];
   const int64_t wpr = Kb / 32;
   const int C = (int)(Kb / 128);  // 16-byte pieces per weight row
   const int nseg = (int)((Kb + kB1Seg - 1) / kB1Seg);
@@ -222,7 +223,6 @@ __global__ __launch_bounds__(64 * kB1Wpb) void mfma1_kernel(
 
   // result lane l, register r of token tile tm: token 16 tm + 4 g + r, weight row nbase + li
   const int64_t n = nbase + li;
-  const float sw = w_scale[0];
 #pragma unroll
   for (int tm = 0; tm < TMS; ++tm)
 #pragma unroll

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
 
   TokenOperands<TM> tok;  // the epilogue's scales and row sums
   tok.load(x_scale, rowsum, M, m0 + 16 * wm * TM);
+  const float ws0 = s0[0], ws1 = NB == 2 ? s1[0] : 0.0f;  // weight scales, also early
 
   // ---- loaders: P chunks of loads in flight, in registers.  Buffer loads
   // issued without branches: rows past M, words past a row's end and chunks
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
   // ---- epilogue (group 0)
   if constexpr (EPI == MF_STORE) {
     if (!owner) return;
-    const float sw = s0[0];
+    const float sw = ws0;
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256 * KS) void mfma_gemm_kernel(
     }
   } else {
     __shared__ float red[WAVES_N][BM];
-    const float sg = s0[0], su = s1[0];
+    const float sg = ws0, su = ws1;
     if (owner) {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
@@ -390,6 +391,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   // rows' scales
   TokenOperands<1> tok;
   tok.load(x_scale, rowsum, M, 0);
+  const float ws0 = s0[0], ws1 = EPI == MF_GATEUP ? s1[0] : 0.0f;  // weight scales
   float xs8[4] = {};
   if constexpr (EPI == MF_A48) {
     const buf_rsrc rx = make_buf_rsrc(x_scale, (uint32_t)(4 * M));
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
   // result lane l, register r: token 4g + r, weight row nbase + li
   const int64_t n = nbase + li;
   if constexpr (EPI == MF_STORE) {
-    const float sw = s0[0];
+    const float sw = ws0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
     // rows m and m + Mh of the tile are token m's int4 and int8 parts; the
     // wave trades its accumulators through its own weight patch (free after
     // the last step) so the lane of row m sees both
-    const float sw = s0[0];
+    const float sw = ws0;
     const int Mh = M / 2;
     int av[4];
 #pragma unroll
@@ -548,7 +550,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_stream_kernel(
                                             ex[(m + Mh) * 16 + li], __fmul_rn(sw, xs8[r]));
     }
   } else {
-    const float sg = s0[0], su = s1[0];
+    const float sg = ws0, su = ws1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;

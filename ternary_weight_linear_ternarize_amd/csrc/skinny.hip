@@ -59,6 +59,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
   // sunk to its store after the weight loads would wait for everything)
   TokenOperands<1> tok;  // the epilogue's scales and row sums, before everything else
   tok.load(x_scale, rowsum, M, 0);
+  const float ws0 = s0[0], ws1 = NB == 2 ? s1[0] : 0.0f;  // weight scales, also early
   const buf_rsrc rx = make_buf_rsrc(Xq, (uint32_t)(M * Kp));
   u32x4 xr[XR];
 #pragma unroll
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
   // result lane l, register r: token 4g + r, weight row nbase + li
   const int64_t n = nbase + li;
   if constexpr (EPI == SK_DSTORE) {
-    const float sw = s0[0];
+    const float sw = ws0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64 * WPB) void mfma_direct_kernel(
       }
     }
   } else {
-    const float sg = s0[0], su = s1[0];
+    const float sg = ws0, su = ws1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * g + r;
