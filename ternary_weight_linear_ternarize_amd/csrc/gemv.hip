@@ -260,16 +260,17 @@ __global__ __launch_bounds__(NT) void gemv_kernel(const GemvArgs a) {
       }
     }
     if constexpr (NORM) {
-      // the norm weights ride with the row (branch-free buffer loads; past
-      // K, or with no weights, they read 0) instead of being fetched after
-      // the mean square
-      const buf_rsrc rw = make_buf_rsrc(a.norm_w, a.norm_w ? (uint32_t)(4 * K) : 0u);
+      // the norm weights (if any) ride with the row, as buffer loads that
+      // read 0 past K, instead of being fetched after the mean square
+      if (a.norm_w) {
+        const buf_rsrc rw = make_buf_rsrc(a.norm_w, (uint32_t)(4 * K));
 #pragma unroll
-      for (int j = 0; j < NWT; ++j)
+        for (int j = 0; j < NWT; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          nwv[j][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rw, (uint32_t)(4 * (4 * (tid + NT * j) + b)), 0, 0));
+          for (int b = 0; b < 4; ++b)
+            nwv[j][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rw, (uint32_t)(4 * (4 * (tid + NT * j) + b)), 0, 0));
+      }
     }
   }
 
