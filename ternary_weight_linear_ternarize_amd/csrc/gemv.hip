@@ -523,7 +523,9 @@ __global__ __launch_bounds__(64 * kPipeWaves) void gemv_pipe_kernel(const GemvAr
         }
       }
     }
+    // float input: the first two row blocks go out before the quantisation
     pipe_issue<KC, R>(a, gw, lane, C, wpr, bA);
+    if constexpr (IT > 1) pipe_issue<KC, R>(a, gw + T, lane, C, wpr, bB);
     __builtin_amdgcn_sched_barrier(0);
     float m = 0.0f;
 #pragma unroll
@@ -566,14 +568,19 @@ __global__ __launch_bounds__(64 * kPipeWaves) void gemv_pipe_kernel(const GemvAr
   }
   const float sc = __fmul_rn(a.s0[0], gx);
   if constexpr (IT > 0) {
-    uint4 (*buf[2])[KC] = {bA, bB};
+    // D row blocks in flight per wave: 3 for float input (the 100B-class
+    // layer from fp32 11.6-11.8 -> 11.0-11.1 us), 2 for int8 codes (3 there
+    // measured 0.1 us slower)
+    constexpr int D = XSRC == XS_INT8 ? 2 : 3;
+    uint4 bC[R][KC];
+    uint4 (*buf[3])[KC] = {bA, bB, bC};
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      if (it + 1 < IT)
-        pipe_issue<KC, R>(a, gw + (it + 1) * T, lane, C, wpr,
-                          *reinterpret_cast<uint4(*)[R][KC]>(buf[(it + 1) & 1]));
+      if (it + D - 1 < IT)
+        pipe_issue<KC, R>(a, gw + (it + D - 1) * T, lane, C, wpr,
+                          *reinterpret_cast<uint4(*)[R][KC]>(buf[(it + D - 1) % 3]));
       __builtin_amdgcn_sched_barrier(0);
-      pipe_rows<KC, R>(a, *reinterpret_cast<uint4(*)[R][KC]>(buf[it & 1]), x, gw + it * T, rsum,
+      pipe_rows<KC, R>(a, *reinterpret_cast<uint4(*)[R][KC]>(buf[it % 3]), x, gw + it * T, rsum,
                        sc);
     }
     return;
