@@ -603,38 +603,41 @@ __device__ double block_sumsq_exact(const float (&xv)[NWT][4], SumsqScratch& sh)
 //
 // Fast path: S_a = the binary64 sum of the squares (each square is exact in
 // binary64) in any order, |S_a - S| <= (n - 1) 2^-53 S <= 2^-37 S for
-// n <= 2^16 non-negative terms, and q_a = RN64(S_a / D).  If q_a is farther
-// than 2^-35 q_a from both binary32 rounding midpoints around c = RN32(q_a),
-// then S / D and every value within 2^-36 of it (the exact route's
-// intermediate binary64 roundings included) round to c, so ms = c.  Otherwise
-// (rows within ~2^-35 of a midpoint, all zero, or at the top of the range)
-// the exact sum decides.
+// n <= 2^16 non-negative terms, and q_a = RN64(S_a * RN64(1 / D)), within
+// 2^-37 + 2^-51 of S / D relatively (the reciprocal is taken before the
+// reduction, off its critical path).  If q_a is farther than 2^-35 q_a from
+// both binary32 rounding midpoints around c = RN32(q_a), then S / D and every
+// value within 2^-36 of it (the exact route's intermediate binary64 roundings
+// included) round to c, so ms = c.  Otherwise (rows within ~2^-35 of a
+// midpoint, all zero, or at the top of the range) the exact sum decides.
 template <int NWT, int NT>
 __device__ float block_meansq(const float (&xv)[NWT][4], int64_t D, SumsqScratch& sh) {
   constexpr int NWV = NT / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  double a = 0.0;
+  const double rD = 1.0 / (double)D;  // off the reduction's critical path
+  double a0 = 0.0, a1 = 0.0;
 #pragma unroll
   for (int j = 0; j < NWT; ++j)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const double x = (double)xv[j][b];
-      a += x * x;
+    for (int b = 0; b < 4; b += 2) {
+      const double x0 = (double)xv[j][b], x1 = (double)xv[j][b + 1];
+      a0 += x0 * x0;
+      a1 += x1 * x1;
     }
-  a = dpp::sum_f64(a);
+  double a = dpp::sum_f64(a0 + a1);
   double* dpart = reinterpret_cast<double*>(&sh.part[0][0]);
   if (lane == 0) dpart[wave] = a;
   __syncthreads();
   a = dpp::sum_f64(lane < NWV ? dpart[lane] : 0.0);
-  const double qa = a / (double)D;
+  const double qa = a * rD;
   const float c = (float)qa;
   // neighbours of c >= 0 (c = 0 gives a NaN below, hence the exact path)
   const uint32_t cb = __float_as_uint(c);
   const double lo = 0.5 * ((double)c + (double)__uint_as_float(cb - 1u));
   const double hi = 0.5 * ((double)c + (double)__uint_as_float(cb + 1u));
   const double tol = qa * 0x1p-35;
-  __syncthreads();  // dpart (sh.part) is reused below
   if (cb < 0x7f7fffffu && qa - lo > tol && hi - qa > tol) return c;  // block-uniform
+  __syncthreads();  // dpart (sh.part) is reused below
   const double s = block_sumsq_exact<NWT, NT>(xv, sh);
   return (float)(s / (double)D);
 }

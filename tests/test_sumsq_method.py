@@ -161,7 +161,7 @@ def meansq_fast(row, rng):
     for v in sq[rng.permutation(len(sq))]:
         a += float(v)
     D = len(row)
-    qa = a / D
+    qa = a * (1.0 / D)  # the kernel multiplies by the binary64 reciprocal
     with np.errstate(over="ignore"):
         c = np.float32(qa)
     cb = int(c.view(np.uint32))
