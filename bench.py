@@ -417,6 +417,18 @@ def main():
                                       "GBps": round(alg_dn / (dn_ms * 1e-3) / 1e9, 1)},
         "decode_step_eager_us": round(eager_ms * 1e3, 3),
     }
+    if not args.no_extra:
+        # the same up layer with its own RMSNorm (norm weights ~1 + 0.1 N(0,1))
+        # in the one kernel: bitlinear_forward_fused_norm
+        nwt = (1.0 + 0.1 * torch.from_numpy(synth.normal(9, 1, (K,)))).float().to(dev)
+        wsn = B.fused_norm_workspace(1, K, dev)
+        upn_ms = graph_time_per_launch(
+            lambda i: B.bitlinear_forward_fused_norm(x, ups[i % copies], sup, N, nwt, 2.0 ** -23,
+                                                     out=y1, ws=wsn),
+            nl, 1, torch)
+        alg_upn = alg_up + K * 4
+        kernels["gemv_fused_norm_up_2560x6912"] = {
+            "avg_us": round(upn_ms * 1e3, 3), "GBps": round(alg_upn / (upn_ms * 1e-3) / 1e9, 1)}
     del ups, dns
     torch.cuda.empty_cache()
 

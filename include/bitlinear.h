@@ -258,6 +258,33 @@ int bitlinear_forward_fused(const void *X, int dtype, int64_t M, int64_t K, cons
                             const float *w_scale, int64_t N, float *Y, void *ws,
                             size_t ws_bytes, void *stream);
 
+/*
+ * bitlinear_forward_fused_norm -- the same with the layer's own RMSNorm in
+ * front of the quantiser: y = BitLinear(RMSNorm(x)), the order of the
+ * BitLinear_b158 forward in [P1] "BitNet b1.58" (normalise, quantise,
+ * multiply, rescale).  Per token r = 1 / sqrt(ms + norm_eps) with
+ * ms = binary32(binary64(exact sum x^2) / K), and xn = (x * r) * norm_w
+ * (norm_w NULL: xn = x * r); the codes, scale and row sum are those of
+ * bitlinear_quant_act on xn.  One float32 token with Kp <= 8192 runs as a
+ * single kernel (every block normalises and quantises the token; identical
+ * bits); otherwise the RMSNorm + quantiser kernel, then bitlinear_forward.
+ *
+ *  X, dtype, M, K, Wp, w_scale, N, Y   as bitlinear_forward_fused.
+ *  norm_w   [K] float32, device, or NULL for ones.  norm_eps: the epsilon
+ *           added to the mean square (torch.nn.RMSNorm's default for float32
+ *           is 2^-23).
+ *  ws       >= bitlinear_fused_norm_workspace_bytes(M, K) bytes, 16-byte
+ *           aligned.  On return it holds what bitlinear_forward_fused leaves
+ *           there (codes, scales, row sums at the same offsets) and xn
+ *           [M][K] float32 at offset bitlinear_fused_workspace_bytes(M, K).
+ *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN (norm_w too), BL_EWORKSPACE, BL_EHIP.
+ */
+size_t bitlinear_fused_norm_workspace_bytes(int64_t M, int64_t K);
+int bitlinear_forward_fused_norm(const void *X, int dtype, int64_t M, int64_t K,
+                                 const float *norm_w, float norm_eps, const uint32_t *Wp,
+                                 const float *w_scale, int64_t N, float *Y, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* Workspace layout of bitnet_ffn_forward.  bitnet_ffn_workspace_layout fills
  * off[BL_FFN_WS_COUNT] with byte offsets (each 256-byte aligned) and returns
  * the total size.  After a call the workspace holds the block's internals:

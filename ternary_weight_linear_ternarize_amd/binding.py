@@ -73,6 +73,10 @@ def lib():
     L.bitlinear_fused_workspace_offset.restype = SZ
     L.bitlinear_forward_fused.argtypes = [P, I, I64, I64, P, P, I64, P, P, SZ, P]
     L.bitlinear_forward_fused.restype = I
+    L.bitlinear_fused_norm_workspace_bytes.argtypes = [I64, I64]
+    L.bitlinear_fused_norm_workspace_bytes.restype = SZ
+    L.bitlinear_forward_fused_norm.argtypes = [P, I, I64, I64, P, F, P, P, I64, P, P, SZ, P]
+    L.bitlinear_forward_fused_norm.restype = I
     L.bitnet_ffn_workspace_layout.argtypes = [I64, I64, I64, P]
     L.bitnet_ffn_workspace_layout.restype = SZ
     L.bitnet_ffn_workspace_bytes.argtypes = [I64, I64, I64]
@@ -370,6 +374,43 @@ def fused_internals(ws, M, K):
     return {"xq": ws[:M * kp].view(torch.int8).reshape(M, kp),
             "x_scale": ws[o1:o1 + 4 * M].view(torch.float32),
             "x_rowsum": ws[o2:o2 + 4 * M].view(torch.int32)}
+
+
+def fused_norm_workspace(M, K, device):
+    n = lib().bitlinear_fused_norm_workspace_bytes(int(M), int(K))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def bitlinear_forward_fused_norm(X, Wp, w_scale, N, norm_w=None, norm_eps=2.0 ** -23, out=None,
+                                 ws=None):
+    """y = BitLinear(RMSNorm(X)) for X [M, K] float32/bfloat16 -> Y [M, N]
+    float32; norm_w a [K] float32 tensor or None (ones).  Returns (Y, ws); ws
+    holds xn, the int8 codes, scales and row sums (see fused_norm_internals)."""
+    M, K = _matrix(X, "X")
+    dt = _act_dtype(X)
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = ws if ws is not None else fused_norm_workspace(M, K, dev)
+    _check_weights(Wp, w_scale, N, K)
+    _check_out(Y, None, M, N)
+    if norm_w is not None:
+        _expect(norm_w, "norm_w", (K,), (torch.float32,))
+    _expect(ws, "ws", min_bytes=lib().bitlinear_fused_norm_workspace_bytes(int(M), int(K)))
+    _same_device(X, Wp, w_scale, Y, ws, norm_w)
+    st = lib().bitlinear_forward_fused_norm(_dev(X, "X"), dt, M, K, _opt(norm_w, "norm_w"),
+                                            float(norm_eps), _dev(Wp, "Wp"),
+                                            _dev(w_scale, "w_scale"), N, _dev(Y, "Y"),
+                                            _dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                            _stream(dev))
+    _check(st, "bitlinear_forward_fused_norm")
+    return Y, ws
+
+
+def fused_norm_internals(ws, M, K):
+    d = fused_internals(ws, M, K)
+    o = lib().bitlinear_fused_workspace_bytes(M, K)
+    d["xn"] = ws[o:o + 4 * M * K].view(torch.float32).reshape(M, K)
+    return d
 
 
 def bitnet_ffn_forward(H, norm_w, norm_eps, Wg, sg, Wu, su, Wd, sd, D, F, out=None, ws=None,

@@ -250,6 +250,39 @@ int bitlinear_forward_fused(const void* X, int dtype, int64_t M, int64_t K, cons
   return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
 }
 
+size_t bitlinear_fused_norm_workspace_bytes(int64_t M, int64_t K) {
+  if (!m_ok(M) || !dim_ok(K)) return 0;
+  return bitlinear_fused_workspace_bytes(M, K) + up256((size_t)M * (size_t)K * 4);
+}
+
+int bitlinear_forward_fused_norm(const void* X, int dtype, int64_t M, int64_t K,
+                                 const float* norm_w, float norm_eps, const uint32_t* Wp,
+                                 const float* w_scale, int64_t N, float* Y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!X || !Wp || !w_scale || !Y) return BL_EINVAL;
+  if (dtype != BL_F32 && dtype != BL_BF16) return BL_EINVAL;
+  if (!m_ok(M) || !dim_ok(K) || !dim_ok(N)) return BL_ESHAPE;
+  if (!ws || ws_bytes < bitlinear_fused_norm_workspace_bytes(M, K)) return BL_EWORKSPACE;
+  if (!aligned(X, dtype == BL_F32 ? 4 : 2) || !aligned(Wp, 16) || !aligned(w_scale, 4) ||
+      !aligned(Y, 4) || !aligned(ws, 16) || (norm_w && !aligned(norm_w, 4)))
+    return BL_EALIGN;
+  char* base = reinterpret_cast<char*>(ws);
+  int8_t* xq = reinterpret_cast<int8_t*>(base);
+  float* xs = reinterpret_cast<float*>(base + bitlinear_fused_workspace_offset(M, K, 1));
+  int32_t* rs = reinterpret_cast<int32_t*>(base + bitlinear_fused_workspace_offset(M, K, 2));
+  float* xn = reinterpret_cast<float*>(base + bitlinear_fused_workspace_bytes(M, K));
+  hipStream_t s = as_stream(stream);
+  const bool bf16 = dtype == BL_BF16;
+  // one float32 token: RMSNorm, quantisation and the product in one kernel
+  if (M == 1 && !bf16 && bl::gemv_norm_ok(K))
+    return hip_status(bl::launch_gemv_norm(reinterpret_cast<const float*>(X), K, norm_w, norm_eps,
+                                           Wp, w_scale, N, Y, xn, xq, xs, rs, s));
+  hipError_t e = bl::launch_rmsnorm_quant(X, bf16, M, K, norm_w, norm_eps, xn, xq, xs, rs, s);
+  if (e != hipSuccess) return BL_EHIP;
+  if (M == 1) return hip_status(bl::launch_gemv(xq, xs, rs, K, Wp, w_scale, N, Y, nullptr, s));
+  return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
+}
+
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off) {
   if (!m_ok(M) || !dim_ok(D) || !dim_ok(F)) return 0;
   const size_t m = (size_t)M;

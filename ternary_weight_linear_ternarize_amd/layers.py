@@ -28,23 +28,34 @@ class BitLinear:
     per-token int8 quantisation, the ternary product and the dequantisation
     (one fused call for the 2-bit layouts).  a48_outliers = n (2-bit layouts
     only) takes the BitNet a4.8 activations instead (youngju.dev "BitNet
-    a4.8"): per token the n largest |x| in 8 bits, the rest in 4 bits."""
+    a4.8"): per token the n largest |x| in 8 bits, the rest in 4 bits.
+    norm=True (ternary and binary 2-bit layouts, int8 activations) puts the
+    layer's own RMSNorm in front of the quantiser, as the BitLinear_b158 forward
+    of youngju.dev "BitNet b1.58" does: norm_weight [K] float32 (None = ones)
+    and norm_eps, all in the same fused call."""
 
-    def __init__(self, weight, mode=B.BL_TERNARY, a48_outliers=None):
+    def __init__(self, weight, mode=B.BL_TERNARY, a48_outliers=None, norm=False,
+                 norm_weight=None, norm_eps=2.0 ** -23):
         if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
             raise ValueError("weight must be a 2-D tensor [out_features, in_features]")
         self.out_features, self.in_features = (int(d) for d in weight.shape)
         self.mode = mode
         if a48_outliers is not None and mode == B.BL_BINARY_1BIT:
             raise ValueError("a4.8 activations run on the 2-bit layouts")
+        if norm and (a48_outliers is not None or mode == B.BL_BINARY_1BIT):
+            raise ValueError("the normalising layer takes int8 activations on the 2-bit layouts")
+        if norm_weight is not None and not norm:
+            raise ValueError("norm_weight needs norm=True")
         self.a48_outliers = a48_outliers
+        self.norm, self.norm_weight, self.norm_eps = norm, norm_weight, norm_eps
         self.weight_packed, self.weight_scale = B.bitlinear_pack(weight.contiguous(), mode)
         self._ws = {}
 
     def _workspace(self, M, device):
         key = (M, device)
         if key not in self._ws:
-            self._ws = {key: B.fused_workspace(M, self.in_features, device)}
+            make = B.fused_norm_workspace if self.norm else B.fused_workspace
+            self._ws = {key: make(M, self.in_features, device)}
         return self._ws[key]
 
     def __call__(self, x):
@@ -56,6 +67,10 @@ class BitLinear:
         elif self.mode == B.BL_BINARY_1BIT:
             Xq, xs, xr = B.bitlinear_quant_act(X)
             Y = B.bitlinear_forward_1bit(Xq, xs, xr, K, self.weight_packed, self.weight_scale, N)
+        elif self.norm:
+            Y, _ = B.bitlinear_forward_fused_norm(X, self.weight_packed, self.weight_scale, N,
+                                                  self.norm_weight, self.norm_eps,
+                                                  ws=self._workspace(X.shape[0], X.device))
         else:
             Y, _ = B.bitlinear_forward_fused(X, self.weight_packed, self.weight_scale, N,
                                              ws=self._workspace(X.shape[0], X.device))

@@ -147,6 +147,30 @@ def test_ffn_validation():
     assert lib.bitnet_ffn_forward(*a) == B.BL_EALIGN
 
 
+def test_fused_norm_validation():
+    lib = B.lib()
+    f = lib.bitlinear_forward_fused_norm
+    M, K, N = 2, 64, 16
+    n = lib.bitlinear_fused_norm_workspace_bytes(M, K)
+    assert n >= lib.bitlinear_fused_workspace_bytes(M, K) + M * K * 4
+    assert lib.bitlinear_fused_norm_workspace_bytes(0, K) == 0
+    base = [FAKE, 0, M, K, None, 1e-6, FAKE, FAKE, N, FAKE, FAKE, n, None]
+    a = list(base); a[0] = None
+    assert f(*a) == B.BL_EINVAL
+    a = list(base); a[1] = 3
+    assert f(*a) == B.BL_EINVAL
+    a = list(base); a[8] = 0
+    assert f(*a) == B.BL_ESHAPE
+    a = list(base); a[11] = n - 1
+    assert f(*a) == B.BL_EWORKSPACE
+    a = list(base); a[10] = None
+    assert f(*a) == B.BL_EWORKSPACE
+    a = list(base); a[4] = ODD  # the norm weights
+    assert f(*a) == B.BL_EALIGN
+    a = list(base); a[6] = ODD
+    assert f(*a) == B.BL_EALIGN
+
+
 def test_product_does_not_reference_the_oracle():
     pkg = os.path.join(ROOT, "ternary_weight_linear_ternarize_amd")
     for dirpath, _, files in os.walk(pkg):

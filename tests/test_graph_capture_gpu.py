@@ -105,6 +105,25 @@ def test_graph_fused_and_plain_forward():
     check_replays(call, [Y1, Y2], [ws, q[0]], checked)
 
 
+@pytest.mark.parametrize("M", [1, 6])
+def test_graph_fused_norm_forward(M):
+    # one token: the normalising GEMV; several: RMSNorm + quantiser, product
+    d = synth.decode_2b()
+    K, N = synth.DECODE_2B["K"], synth.DECODE_2B["N"]
+    Wp, sc = B.bitlinear_pack(to_dev(d["W_up"]))
+    X = to_dev(synth.normal(6, 1, (M, K)))
+    nw = to_dev((1.0 + 0.1 * synth.normal(6, 2, (K,))).astype(np.float32))
+    ws = B.fused_norm_workspace(M, K, DEV)
+    Y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+
+    def call():
+        B.bitlinear_forward_fused_norm(X, Wp, sc, N, nw, 1e-6, out=Y, ws=ws)
+
+    inner = B.fused_norm_internals(ws, M, K)
+    checked = [Y] + [inner[k] for k in sorted(inner)]
+    check_replays(call, [Y], [ws], checked)
+
+
 def test_graph_1bit_and_a48():
     d = synth.random_case(606, 8, 3000, 700)
     K, N = 3000, 700

@@ -70,6 +70,25 @@ def test_bitlinear_layer_a48_matches_oracle():
         layers.BitLinear(_dev(W), B.BL_BINARY_1BIT, a48_outliers=7)
 
 
+@pytest.mark.parametrize("mode,with_w", [(B.BL_TERNARY, True), (B.BL_BINARY, False)])
+def test_bitlinear_layer_with_its_norm_matches_oracle(mode, with_w):
+    W = synth.normal(74, 1, (333, 640))
+    X = synth.normal(74, 2, (3, 640))
+    nw = (np.float32(1) + synth.normal(74, 3, (640,), 0.1)).astype(np.float32) if with_w else None
+    layer = layers.BitLinear(_dev(W), mode, norm=True,
+                             norm_weight=_dev(nw) if with_w else None, norm_eps=1e-6)
+    g, t, _ = oracle.quantize_weights(W, "ternary" if mode == B.BL_TERNARY else "binary")
+    for x in (X, X[:1]):  # several tokens, and one (the one-kernel path)
+        xn = oracle.rmsnorm(x, nw, 1e-6)
+        q, gx, _ = oracle.act_quant(xn)
+        ref = oracle.dequant(oracle.int_linear(q, t), gx, g)
+        assert _rel(_host(layer(_dev(x))), ref) <= 1e-5
+    with pytest.raises(ValueError):
+        layers.BitLinear(_dev(W), B.BL_BINARY_1BIT, norm=True)
+    with pytest.raises(ValueError):
+        layers.BitLinear(_dev(W), norm_weight=_dev(np.ones(640, np.float32)))
+
+
 @pytest.mark.parametrize("subln", [False, True])
 def test_ffn_layer_matches_oracle(subln):
     D, F = 256, 600

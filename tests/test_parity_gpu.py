@@ -533,6 +533,61 @@ def test_forward_fused_from_float(M, K, N, bf16):
     np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
 
 
+@pytest.mark.parametrize("M,K,N,bf16,nw,eps", [
+    # one float32 token: the normalising GEMV (one and two chunks per lane)
+    (1, 2560, 6912, False, True, 2.0 ** -23), (1, 6912, 2560, False, False, 2.0 ** -23),
+    (1, 8192, 300, False, True, 1e-6), (1, 1, 5, False, True, 2.0 ** -23),
+    (1, 4097, 1001, False, False, 1e-5), (1, 8192, 28672, False, True, 2.0 ** -23),
+    # bfloat16 or K past 8192: RMSNorm + quantiser, then the GEMV
+    (1, 6912, 2560, True, True, 2.0 ** -23), (1, 8200, 100, False, True, 1e-6),
+    (1, 65536, 40, False, True, 2.0 ** -23),
+    # several tokens: RMSNorm + quantiser, then the MFMA products
+    (3, 700, 130, True, True, 1e-5), (8, 2560, 6912, False, True, 2.0 ** -23),
+    (64, 2560, 6912, False, False, 2.0 ** -23), (80, 512, 200, True, True, 2.0 ** -23)])
+def test_forward_fused_norm(M, K, N, bf16, nw, eps):
+    d = synth.random_case(3500 + K + N, M, K, N)
+    X = synth.with_outliers(d["X"], synth.outlier_columns(3500 + K, K)) if K > 100 else d["X"]
+    g, t, Wp, sc = check_pack(d["W"])
+    xd = to_dev(X)
+    if bf16:
+        xd = xd.to(torch.bfloat16)
+        X = xd.float().cpu().numpy()
+    w = (1.0 + 0.1 * synth.normal(3500, K, (K,))).astype(np.float32) if nw else None
+    xn = oracle.rmsnorm(X, w, eps)
+    q, gx, rs = oracle.act_quant(xn)
+    acc = oracle.int_linear(q, t)
+    y = oracle.dequant(acc, gx, g)
+    wd = to_dev(w) if nw else None
+    Y, ws = B.bitlinear_forward_fused_norm(xd, Wp, sc, N, wd, eps)
+    it = {k: host(v) for k, v in B.fused_norm_internals(ws, M, K).items()}
+    np.testing.assert_array_equal(it["xn"].view(np.uint32), xn.view(np.uint32))
+    np.testing.assert_array_equal(it["xq"][:, :K], q)
+    assert not it["xq"][:, K:].any()
+    np.testing.assert_array_equal(it["x_scale"].view(np.uint32), gx.view(np.uint32))
+    np.testing.assert_array_equal(it["x_rowsum"], rs)
+    assert_rel(host(Y), y)
+    Y2, _ = B.bitlinear_forward_fused_norm(xd, Wp, sc, N, wd, eps)
+    np.testing.assert_array_equal(host(Y2).view(np.uint32), host(Y).view(np.uint32))
+
+
+def test_forward_fused_norm_rows_at_mean_square_midpoints():
+    # one token and several: rows whose exact mean square is a binary32
+    # rounding midpoint or next to one (the exact sum decides them)
+    K, N = 2560, 700
+    W = synth.normal(3600, 1, (N, K), 0.02)
+    g, t, Wp, sc = check_pack(W)
+    for M in (1, 6):
+        X = synth.midpoint_rows(K, M, 3600 + M)
+        xn = oracle.rmsnorm(X, None, 2.0 ** -23)
+        q, gx, rs = oracle.act_quant(xn)
+        y = oracle.dequant(oracle.int_linear(q, t), gx, g)
+        Y, ws = B.bitlinear_forward_fused_norm(to_dev(X), Wp, sc, N)
+        it = {k: host(v) for k, v in B.fused_norm_internals(ws, M, K).items()}
+        np.testing.assert_array_equal(it["xn"].view(np.uint32), xn.view(np.uint32))
+        np.testing.assert_array_equal(it["xq"][:, :K], q)
+        assert_rel(host(Y), y)
+
+
 # ----------------------------------------------------------------------------
 # binary weights in the 1-bit layout
 
