@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbitlinear.so")
 
-SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "bin1.hip", "a48.hip", "skinny.hip", "probe.hip"]
+SOURCES = ["api.hip", "pack.hip", "quant.hip", "gemv.hip", "gemm.hip", "bin1.hip", "a48.hip", "skinny.hip", "ksplit.hip", "probe.hip"]
 HEADERS = ["bl_device.h", "bl_launch.h", "gemm_tiles.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -714,6 +714,8 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
+  // 17..64 tokens with long K: K split over the waves of a block
+  if (ksplit_ok(M, K, N, 1)) return launch_ksplit(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   // 17 <= M <= 64: 32 x 32 block tiles (four 16 x 16 wave tiles) keep more
   // blocks in flight than 64-row tiles for these weight-streaming shapes,
   // with 2 chunks of loads in flight per wave; long K split over 4 groups of
@@ -785,6 +787,9 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
   // 17 <= M <= 64: 32 x 32 block tiles with 2 chunks of loads in flight
   // (the FFN at 64 tokens 35.2 us against 38.2 with 64 x 16 tiles and one
   // chunk in flight, at 32 tokens 28.7 against 33.7)
+  // 17..32 tokens: K split over the waves of a block
+  if (ksplit_ok(M, K, N, 2))
+    return launch_ksplit_gateup(Xq, xs, rs, M, K, Wg, sg, Wu, su, N, H, gh_parts, nparts, s);
   if (M <= 64)
     return mfma_launch<1, 1, 2, 2, MF_GATEUP, 2>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                                  gh_parts, nparts, s);

@@ -1,0 +1,297 @@
+// Ternary x int8 product for 17..64 tokens with K split over every wave of
+// the block and every load of a wave issued before the first MFMA.
+//
+// youngju.dev "BitNet論文分析", section "BitNet b1.58": the integer product is
+// F.linear(x_q, w_q) followed by output * (w_scale * x_scale) / Q; here in
+// the shifted-code form acc = sum_k q[m][k] * (t[n][k] + 1) - rowsum[m] on
+// v_mfma_i32_16x16x64_i8 (dashen-tech "BitNet.cpp 深度解析" §3.1: the
+// product equals sum_pos - sum_neg).
+//
+// At these token counts a layer moves a few MB (the 2B-class FFN at 64
+// tokens: 8.8 MB of gate/up weights, 160 KB of activation codes), so its time
+// is set by how many bytes each CU has in flight, not by the matrix cores.
+// A block owns a BM x BN output tile (BM = 16 TM tokens, BN = 16 TN columns
+// of each of NB weight matrices) and its W waves split K between them: K is
+// cut into pieces of 128, wave w takes pieces [w ppw, (w + 1) ppw), and all
+// of them -- activation rows and weight words -- are loaded into registers
+// at once, as branch-free buffer loads (rows past M or N and pieces past Kp
+// read zero).  The MFMAs of piece j then wait only for piece j's loads.  The
+// W partial tiles are added through LDS and the block's threads share the
+// epilogue.
+//
+// Operand mapping, lane l = 16 g + li: in piece h, lane group g owns weights
+// 128 h + 32 g .. +31, i.e. packed words 8 h + 2 g and 8 h + 2 g + 1 of a row
+// (word j holds weights 16 j .. 16 j + 15, codes_operand unpacks them in
+// order), one 8-byte load per row; step s (0, 1) feeds word 8 h + 2 g + s of
+// column row li and the 16 activation bytes at 128 h + 32 g + 16 s of token
+// row li.  Result lane l, register r holds (token 4 g + r, column li).
+#include "bl_device.h"
+#include "bl_launch.h"
+
+namespace bl {
+
+enum { KS_STORE = 0, KS_GATEUP = 1 };
+
+constexpr int kPiece = 128;  // K per piece
+
+template <int NB, int TM, int TN, int W, int CPW, int EPI>
+__global__ __launch_bounds__(64 * W) void mfma_ksplit_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ rowsum, int64_t M, int64_t Kp,
+    const uint32_t* __restrict__ W0, const float* __restrict__ s0,
+    const uint32_t* __restrict__ W1, const float* __restrict__ s1, int64_t N,
+    float* __restrict__ Y, int32_t* __restrict__ acc_out, float* __restrict__ gh_parts, int nbn,
+    int ppw) {
+  constexpr int BM = 16 * TM, BN = 16 * TN;
+  constexpr int J = NB * TM * TN;  // accumulator tiles per wave
+  constexpr int NT = 64 * W;
+  extern __shared__ __attribute__((aligned(16))) v4i ks_lds[];
+  v4i* part = ks_lds;                                              // [W][J][64]
+  float* tokx = reinterpret_cast<float*>(ks_lds + W * J * 64);     // [BM]
+  int* tokr = reinterpret_cast<int*>(tokx + BM);                   // [BM]
+  uint32_t* hred = reinterpret_cast<uint32_t*>(tokr + BM);         // [BM]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  const int bid = __builtin_amdgcn_readfirstlane(blockIdx.x);
+  const int bn = bid % nbn, bm = bid / nbn;
+  const int64_t m0 = (int64_t)bm * BM, n0 = (int64_t)bn * BN;
+  const int64_t wpr = Kp / 16;
+  const int64_t npieces = (Kp + kPiece - 1) / kPiece;
+  const int64_t h0 = (int64_t)wave * ppw;
+  const int64_t hn = npieces - h0 < ppw ? npieces - h0 : ppw;  // pieces of this wave (may be <= 0)
+
+  // the epilogue's per-token operands, early (tokens past M read 0)
+  float tx = 0.0f;
+  int tr = 0;
+  if (tid < BM) {
+    const buf_rsrc rx = make_buf_rsrc(x_scale, (uint32_t)(4 * M));
+    const buf_rsrc rr = make_buf_rsrc(rowsum, (uint32_t)(4 * M));
+    const uint32_t off = m0 + tid < M ? (uint32_t)(4 * (m0 + tid)) : 0x80000000u;
+    tx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+    tr = (int)__builtin_amdgcn_raw_buffer_load_b32(rr, off, 0, 0);
+  }
+  const float ws0 = s0[0], ws1 = NB == 2 ? s1[0] : 0.0f;
+
+  const int64_t mrows = M - m0 < BM ? M - m0 : BM;
+  const int64_t nrows = N - n0 < BN ? N - n0 : BN;
+  const buf_rsrc ra = make_buf_rsrc(Xq + m0 * Kp, (uint32_t)(mrows * Kp));
+  const buf_rsrc rb0 = make_buf_rsrc(W0 + n0 * wpr, (uint32_t)(nrows * wpr * 4));
+  const buf_rsrc rb1 = make_buf_rsrc((NB == 2 ? W1 : W0) + n0 * wpr, (uint32_t)(nrows * wpr * 4));
+
+  // ---- every load of the wave, piece by piece
+  u32x4 a_reg[CPW][TM][2];
+  uint32_t b_reg[CPW][NB][TN][2];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int64_t h = h0 + j;
+    const bool live = j < hn;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int64_t k = kPiece * h + 32 * g + 16 * s;
+        const uint32_t off =
+            live && k < Kp ? (uint32_t)((16 * tm + li) * Kp + k) : 0x80000000u;
+        a_reg[j][tm][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+      }
+    }
+    const int64_t word = 8 * h + 2 * g;
+#pragma unroll
+    for (int mat = 0; mat < NB; ++mat) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const uint32_t off = live && word < wpr
+                                 ? (uint32_t)(((16 * tn + li) * wpr + word) * 4)
+                                 : 0x80000000u;
+        const uint2 v = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(mat == 0 ? rb0 : rb1, off, 0, 0));
+        b_reg[j][mat][tn][0] = v.x;
+        b_reg[j][mat][tn][1] = v.y;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  v4i acc[NB][TM][TN];
+#pragma unroll
+  for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) acc[mat][tm][tn] = v4i{0, 0, 0, 0};
+
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    if (j < hn) {  // uniform over the wave
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int mat = 0; mat < NB; ++mat) {
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const v4i b = codes_operand(b_reg[j][mat][tn][s]);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+              acc[mat][tm][tn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  __builtin_bit_cast(v4i, a_reg[j][tm][s]), b, acc[mat][tm][tn], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- the W partial tiles meet in LDS
+#pragma unroll
+  for (int mat = 0; mat < NB; ++mat)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        part[(wave * J + (mat * TM + tm) * TN + tn) * 64 + lane] = acc[mat][tm][tn];
+  if (tid < BM) {
+    tokx[tid] = tx;
+    tokr[tid] = tr;
+    hred[tid] = 0u;
+  }
+  __syncthreads();
+
+  // ---- epilogue: slot = (tm, tn, lane) of the tile, all NB matrices
+  constexpr int SLOTS = TM * TN * 64;
+  for (int slot = tid; slot < SLOTS; slot += NT) {  // the same trip count for a whole wave
+    const int sl = slot & 63, jt = slot >> 6;
+    const int tm = jt / TN, tn = jt % TN;
+    const int sg = sl >> 4, sli = sl & 15;
+    v4i sum[NB];
+#pragma unroll
+    for (int mat = 0; mat < NB; ++mat) {
+      v4i t = part[((mat * TM + tm) * TN + tn) * 64 + sl];
+#pragma unroll
+      for (int w = 1; w < W; ++w) t += part[(w * J + (mat * TM + tm) * TN + tn) * 64 + sl];
+      sum[mat] = t;
+    }
+    const int64_t n = n0 + 16 * tn + sli;
+    if constexpr (EPI == KS_STORE) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = 16 * tm + 4 * sg + r;
+        const int64_t m = m0 + lrow;
+        if (m < M && n < N) {
+          const int a = sum[0][r] - tokr[lrow];
+          if (Y) Y[m * N + n] = dequant_fast(a, __fmul_rn(ws0, tokx[lrow]));
+          if (acc_out) acc_out[m * N + n] = a;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = 16 * tm + 4 * sg + r;
+        const int64_t m = m0 + lrow;
+        float hm = 0.0f;
+        if (m < M && n < N) {
+          const int rsm = tokr[lrow];
+          const float xs = tokx[lrow];
+          const float gv = dequant_fast(sum[0][r] - rsm, __fmul_rn(ws0, xs));
+          const float uv = dequant_fast(sum[1][r] - rsm, __fmul_rn(ws1, xs));
+          const float rl = gv > 0.0f ? gv : 0.0f;
+          const float hv = __fmul_rn(__fmul_rn(rl, rl), uv);
+          Y[m * N + n] = hv;
+          hm = fabsf(hv);
+          hm = hm == hm ? hm : 0.0f;  // a NaN h does not enter the maximum
+        }
+        // max over the 16 lanes holding this token row
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) hm = fmaxf(hm, __shfl_xor(hm, o));
+        if (sli == 0 && hm > 0.0f) atomicMax(&hred[lrow], __float_as_uint(hm));
+      }
+    }
+  }
+  if constexpr (EPI == KS_GATEUP) {
+    __syncthreads();
+    if (tid < BM && m0 + tid < M) gh_parts[(int64_t)bn * M + m0 + tid] = __uint_as_float(hred[tid]);
+  }
+}
+
+template <int NB, int TM, int TN, int W, int CPW, int EPI>
+static hipError_t ksplit_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                            int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
+                            const float* s1, int64_t N, float* Y, int32_t* acc_out,
+                            float* gh_parts, int* nparts, int ppw, hipStream_t s) {
+  constexpr int BM = 16 * TM, BN = 16 * TN;
+  const int64_t nbm = (M + BM - 1) / BM, nbn = (N + BN - 1) / BN;
+  const size_t lds = (size_t)W * NB * TM * TN * 64 * 16 + 3 * 4 * BM;
+  static bool once = ((void)hipFuncSetAttribute(
+                          reinterpret_cast<const void*>(mfma_ksplit_kernel<NB, TM, TN, W, CPW, EPI>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds),
+                      true);
+  (void)once;
+  if (nparts) *nparts = (int)nbn;
+  hipLaunchKernelGGL((mfma_ksplit_kernel<NB, TM, TN, W, CPW, EPI>), dim3((unsigned)(nbm * nbn)),
+                     dim3(64 * W), lds, s, Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out,
+                     gh_parts, (int)nbn, ppw);
+  return hipGetLastError();
+}
+
+constexpr int kKsWaves = 8;      // waves per block
+static int ks_ppw(int64_t Kp) {
+  return (int)(((Kp + kPiece - 1) / kPiece + kKsWaves - 1) / kKsWaves);
+}
+
+// Pieces per wave held in registers: the smallest instance that covers Kp
+// (at most 8: 24 VGPRs of loads per piece for the gate/up tile).
+template <int NB, int TM, int TN, int EPI>
+static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                             int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
+                             const float* s1, int64_t N, float* Y, int32_t* acc_out,
+                             float* gh_parts, int* nparts, hipStream_t s) {
+  const int ppw = ks_ppw(Kp);
+#define BL_KS_GO(C)                                                                          \
+  if (ppw <= (C))                                                                            \
+  return ksplit_go<NB, TM, TN, kKsWaves, (C), EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y,  \
+                                                   acc_out, gh_parts, nparts, ppw, s)
+  BL_KS_GO(1);
+  BL_KS_GO(2);
+  BL_KS_GO(3);
+  BL_KS_GO(4);
+  BL_KS_GO(5);
+  BL_KS_GO(6);
+  BL_KS_GO(7);
+  BL_KS_GO(8);
+#undef BL_KS_GO
+  return hipErrorInvalidValue;
+}
+
+// Where this kernel measured faster than the 32 x 32 block-tile kernel (same
+// box, bit-identical results): plain products with long K (the 2B-class
+// 6912 -> 2560 layer at 17 / 32 / 64 tokens 9.4 / 10.3 / 10.1 us against
+// 10.3 / 11.1 / 10.8, kernel trace) on 16 x 48 tiles, and the FFN's gate/up
+// up to 32 tokens (2560 -> 2 x 6912: 8.9 / 9.5 us against 10.1 / 10.2) on
+// 32 x 32 tiles of both matrices.  Short-K products (2560 -> 6912: 7.2-8.3
+// against 6.7-8.2 us) and gate/up at 48 and 64 tokens (12.1-12.3 against
+// 11.9-12.0 us, also with 32 x 64 tiles) stay on the block-tile kernel.
+bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
+  (void)N;
+  const int64_t Kp = (K + 63) / 64 * 64;
+  if (M < 17 || ks_ppw(Kp) > 8) return false;
+  return nb == 2 ? M <= 32 : (M <= 64 && Kp >= 4096);
+}
+
+hipError_t launch_ksplit(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                         int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                         int32_t* acc_out, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  return ksplit_cpw<1, 1, 3, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
+                                       nullptr, nullptr, s);
+}
+
+hipError_t launch_ksplit_gateup(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                                int64_t K, const uint32_t* Wg, const float* sg,
+                                const uint32_t* Wu, const float* su, int64_t N, float* H,
+                                float* gh_parts, int* nparts, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  return ksplit_cpw<2, 2, 2, KS_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                        gh_parts, nparts, s);
+}
+
+}  // namespace bl

@@ -124,6 +124,9 @@ def test_single_layer_512_to_400_all_kernels():
     # 17..64 tokens on the skinny tiled GEMM with 2 or 4 chunks of loads in
     # flight: partial last chunks, chunk counts not multiples of the depth
     (48, 3000, 77), (64, 4100, 50), (20, 8000, 33), (64, 7000, 40), (64, 9000, 20),
+    # 17..64 tokens with long K on the kernel that splits K over the waves of a
+    # block: ragged 16-token and 48-column tiles, the most pieces per wave (8)
+    (17, 6912, 100), (33, 8192, 2600), (64, 4096, 2561), (40, 8100, 47),
     # one token, packed matrix >= 16 MiB (the streaming GEMV), ragged K and odd N
     (1, 5000, 13301), (1, 4000, 17001), (1, 8192, 16385), (1, 8192, 8192), (1, 8192, 12001),
     (1, 4096, 40000),
@@ -416,6 +419,10 @@ def test_ffn_2b_subln(M):
                                          (1, 17000, 100, False), (1, 300, 9000, False),
                                          (1, 17000, 100, True),
                                          (17, 512, 1000, False), (40, 1000, 3000, False),
+                                         # gate/up at 17..32 tokens with K split over the
+                                         # waves of a block: 1 to 5 pieces per wave
+                                         (32, 2560, 6912, False), (24, 1000, 3000, True),
+                                         (17, 4100, 900, False), (31, 120, 70, False),
                                          (100, 256, 520, False), (256, 512, 1024, False),
                                          (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
                                          (100, 256, 520, True),
