@@ -131,7 +131,7 @@ hipError_t launch_direct_gateup(const int8_t* Xq, const float* x_scale, const in
                                 const uint32_t* Wu, const float* su, int64_t N, float* H,
                                 float* gh_parts, int* nparts, hipStream_t s);
 
-// 17..64 tokens with K split over the 8 waves of a block and every load of a
+// 2..64 tokens with K split over the 8 waves of a block and every load of a
 // wave in flight at once (ksplit.hip); ksplit_ok says whether K fits the
 // register budget of the tile the shape would take (nb: 1 plain, 2 gate/up).
 bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb);

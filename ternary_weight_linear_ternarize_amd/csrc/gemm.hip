@@ -703,6 +703,8 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
   if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
+  // K split over the waves of a block, where that measured faster (ksplit_ok)
+  if (ksplit_ok(M, K, N, 1)) return launch_ksplit(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   // large layers: the streaming kernel with 7- or 8-wave blocks (activations
   // staged in phases when they do not fit), 18.5 us against the direct
   // kernel's 39.5 us on the 100B-class layer at 16 tokens
@@ -714,8 +716,6 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
   if (M <= 16)
     return mfma_launch<1, 1, 1, 4, MF_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                              acc_out, nullptr, nullptr, s);
-  // 17..64 tokens with long K: K split over the waves of a block
-  if (ksplit_ok(M, K, N, 1)) return launch_ksplit(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   // 17 <= M <= 64: 32 x 32 block tiles (four 16 x 16 wave tiles) keep more
   // blocks in flight than 64-row tiles for these weight-streaming shapes,
   // with 2 chunks of loads in flight per wave; long K split over 4 groups of

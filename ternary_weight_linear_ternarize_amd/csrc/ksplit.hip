@@ -1,4 +1,4 @@
-// Ternary x int8 product for 17..64 tokens with K split over every wave of
+// Ternary x int8 product for 2..64 tokens with K split over every wave of
 // the block and every load of a wave issued before the first MFMA.
 //
 // youngju.dev "BitNet論文分析", section "BitNet b1.58": the integer product is
@@ -262,25 +262,35 @@ static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* r
   return hipErrorInvalidValue;
 }
 
-// Where this kernel measured faster than the 32 x 32 block-tile kernel (same
-// box, bit-identical results): plain products with long K (the 2B-class
-// 6912 -> 2560 layer at 17 / 32 / 64 tokens 9.4 / 10.3 / 10.1 us against
-// 10.3 / 11.1 / 10.8, kernel trace) on 16 x 48 tiles, and the FFN's gate/up
-// up to 32 tokens (2560 -> 2 x 6912: 8.9 / 9.5 us against 10.1 / 10.2) on
-// 32 x 32 tiles of both matrices.  Short-K products (2560 -> 6912: 7.2-8.3
-// against 6.7-8.2 us) and gate/up at 48 and 64 tokens (12.1-12.3 against
-// 11.9-12.0 us, also with 32 x 64 tiles) stay on the block-tile kernel.
+// Where this kernel measured faster than the kernels it replaces (same box,
+// bit-identical results):
+// - 17..64 tokens, plain products with long K, on 16 x 48 tiles: the 2B-class
+//   6912 -> 2560 layer at 17 / 32 / 64 tokens 9.4 / 10.3 / 10.1 us against
+//   10.3 / 11.1 / 10.8 for the 32 x 32 block-tile kernel (kernel trace);
+// - 2..16 tokens, plain products with K <= 4096 and 4096..16384 columns, on
+//   16 x 32 tiles: 2560 -> 6912 at 2 / 8 / 16 tokens 4.3 / 4.9 / 5.3 us
+//   against 4.7 / 5.5 / 6.3 for the direct and streaming kernels (events);
+// - the FFN's gate/up at 17..32 tokens on 32 x 32 tiles of both matrices
+//   (2560 -> 2 x 6912: 8.9 / 9.5 us against 10.1 / 10.2).
+// Measured slower and left to the other kernels: 2560 -> 6912 at 17..64
+// tokens (7.2-8.3 against 6.7-8.2 us), 6912 -> 2560 at 8 and 16 tokens (5.9 /
+// 7.0 against 5.6 / 6.3 us), gate/up at 2..16 tokens (the FFN block 1.2-1.6 us
+// slower) and at 48..64 tokens (12.1-12.3 against 11.9-12.0 us).
 bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
-  (void)N;
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (M < 17 || ks_ppw(Kp) > 8) return false;
-  return nb == 2 ? M <= 32 : (M <= 64 && Kp >= 4096);
+  if (M < 2 || M > 64 || ks_ppw(Kp) > 8) return false;
+  if (nb == 2) return M >= 17 && M <= 32;
+  if (M <= 16) return Kp <= 4096 && N >= 4096 && N <= 16384;
+  return Kp >= 4096;
 }
 
 hipError_t launch_ksplit(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
+  if (M <= 16)
+    return ksplit_cpw<1, 1, 2, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
+                                         acc_out, nullptr, nullptr, s);
   return ksplit_cpw<1, 1, 3, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
                                        nullptr, nullptr, s);
 }
