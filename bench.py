@@ -460,7 +460,8 @@ def main():
 
 
 def extra_workloads(torch, B, synth, dev):
-    """Kernel timings of the other shapes (prefill GEMM, 100B-class decode, FFN),
+    """Kernel timings of the other shapes (prefill GEMM, skinny 2..64-token products,
+    100B-class decode, FFN),
     each from HIP events around graph replays of back-to-back launches."""
     res = {}
     # prefill GEMM: M=2048, K=2560, N=6912
@@ -482,6 +483,26 @@ def extra_workloads(torch, B, synth, dev):
     res["act_quant_2048x2560"] = {"avg_us": round(qa_ms * 1e3, 2),
                                   "GBps": round(M * (K * 5 + 8) / (qa_ms * 1e-3) / 1e9, 1)}
     del copies, Y, X, q, Wp
+    torch.cuda.empty_cache()
+
+    # skinny products on the 2B-class shapes: 2..64 tokens from int8 codes,
+    # rotating weight copies (> 512 MB)
+    d2 = synth.decode_2b()
+    for name, K, N in (("W_up", 2560, 6912), ("W_down", 6912, 2560)):
+        Wp, sc = B.bitlinear_pack(torch.from_numpy(d2[name]).to(dev))
+        ncp = max(2, int(np.ceil(600e6 / (Wp.numel() * 4))))
+        cps = [Wp.clone() for _ in range(ncp)]
+        for M in (2, 8, 16, 32, 64):
+            q = B.bitlinear_quant_act(torch.from_numpy(synth.normal(9, M, (M, K))).to(dev))
+            Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            ms = graph_time_per_launch(
+                lambda i: B.bitlinear_forward(q[0], q[1], q[2], K, cps[i % ncp], sc, N, out=Y),
+                ncp, 5, torch)
+            res[f"forward_{K}x{N}_M{M}"] = {
+                "avg_us": round(ms * 1e3, 2),
+                "weight_GBps": round(Wp.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
+        del cps, Wp
+    del d2
     torch.cuda.empty_cache()
 
     # 100B-class decode: K=8192, N=28672, M in {1, 8}
