@@ -266,7 +266,8 @@ static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* r
 // bit-identical results):
 // - 17..64 tokens, plain products with long K, on 16 x 48 tiles: the 2B-class
 //   6912 -> 2560 layer at 17 / 32 / 64 tokens 9.4 / 10.3 / 10.1 us against
-//   10.3 / 11.1 / 10.8 for the 32 x 32 block-tile kernel (kernel trace);
+//   10.3 / 11.1 / 10.8 for the 32 x 32 block-tile kernel (kernel trace), and
+//   faster still on 16 x 32 tiles where those fit one block per CU (below);
 // - 2..16 tokens, plain products with K <= 4096 and 4096..16384 columns, on
 //   16 x 32 tiles: 2560 -> 6912 at 2 / 8 / 16 tokens 4.3 / 4.9 / 5.3 us
 //   against 4.7 / 5.5 / 6.3 for the direct and streaming kernels (events);
@@ -288,7 +289,12 @@ hipError_t launch_ksplit(const int8_t* Xq, const float* xs, const int32_t* rs, i
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (M <= 16)
+  // 16 x 32 tiles while they fit one block per CU, else 16 x 48 (6912 -> 2560
+  // at 17 / 32 / 48 tokens 7.6 / 8.4 / 8.4 us on 16 x 32 tiles against 9.2 /
+  // 10.2 / 10.2 on 16 x 48; at 64 tokens, 320 blocks of 16 x 32, 12.7 against
+  // 10.3 us)
+  const int64_t nbm = (M + 15) / 16;
+  if (nbm * ((N + 31) / 32) <= 256)
     return ksplit_cpw<1, 1, 2, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
                                          acc_out, nullptr, nullptr, s);
   return ksplit_cpw<1, 1, 3, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
