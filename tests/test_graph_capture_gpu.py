@@ -62,7 +62,8 @@ def check_replays(call, outputs, scratch, checked):
             same_bits(a, b)
 
 
-@pytest.mark.parametrize("M,subln", [(1, False), (8, False), (64, False), (1, True), (8, True)])
+@pytest.mark.parametrize("M,subln", [(1, False), (8, False), (32, False), (64, False), (1, True),
+                                     (8, True)])
 def test_graph_ffn(M, subln):
     f = synth.ffn_2b()
     D, F = synth.FFN_2B["D"], synth.FFN_2B["F"]
@@ -94,15 +95,20 @@ def test_graph_fused_and_plain_forward():
     X = to_dev(synth.normal(5, 1, (40, K)))
     q = B.bitlinear_quant_act(X)
     Y2 = torch.empty((40, N), dtype=torch.float32, device=DEV)
+    X8 = to_dev(synth.normal(6, 1, (8, K)))  # 8 tokens: K split over the waves of a block
+    q8 = B.bitlinear_quant_act(X8)
+    Y3 = torch.empty((8, N), dtype=torch.float32, device=DEV)
 
     def call():
         B.bitlinear_forward_fused(x, Wp, sc, N, out=Y1, ws=ws)
         B.bitlinear_quant_act(X, out=q)
         B.bitlinear_forward(q[0], q[1], q[2], K, Wp, sc, N, out=Y2)
+        B.bitlinear_quant_act(X8, out=q8)
+        B.bitlinear_forward(q8[0], q8[1], q8[2], K, Wp, sc, N, out=Y3)
 
     inner = B.fused_internals(ws, 1, K)
-    checked = [Y1, Y2, q[0], q[1], q[2]] + [inner[k] for k in sorted(inner)]
-    check_replays(call, [Y1, Y2], [ws, q[0]], checked)
+    checked = [Y1, Y2, Y3, q[0], q[1], q[2], q8[0]] + [inner[k] for k in sorted(inner)]
+    check_replays(call, [Y1, Y2, Y3], [ws, q[0], q8[0]], checked)
 
 
 @pytest.mark.parametrize("M", [1, 6])
