@@ -720,6 +720,9 @@ def check_a48(X, n_out, t, g, Wp, sc, bf16=False):
     (1, 16448, 33, 165, False), (3, 700, 130, 7, False), (16, 512, 400, 5, False),
     (64, 2560, 96, 26, True), (100, 1040, 257, 10, False), (1, 40000, 9, 400, False),
     (2, 20000, 17, 200, False), (1, 65536, 40, 655, False), (3, 65536, 24, 100, True),
+    # one token on packed matrices of 16 MiB or more: one and two chunks per
+    # lane, ragged K and N
+    (1, 4000, 17001, 40, False), (1, 8192, 8192, 82, True), (1, 5000, 13301, 50, False),
 ])
 def test_a48_quant_and_forward(M, K, N, n_out, bf16):
     d = synth.random_case(5000 + K + N + M, M, K, N)
