@@ -12,7 +12,7 @@
 // is set by how many bytes each CU has in flight, not by the matrix cores.
 // A block owns a BM x BN output tile (BM = 16 TM tokens, BN = 16 TN columns
 // of each of NB weight matrices) and its W waves split K between them: K is
-// cut into pieces of 128, wave w takes pieces [w ppw, (w + 1) ppw), and all
+// cut into pieces of 256, wave w takes pieces [w ppw, (w + 1) ppw), and all
 // of them -- activation rows and weight words -- are loaded into registers
 // at once, as branch-free buffer loads (rows past M or N and pieces past Kp
 // read zero).  The MFMAs of piece j then wait only for piece j's loads.  The
@@ -20,11 +20,14 @@
 // epilogue.
 //
 // Operand mapping, lane l = 16 g + li: in piece h, lane group g owns weights
-// 128 h + 32 g .. +31, i.e. packed words 8 h + 2 g and 8 h + 2 g + 1 of a row
-// (word j holds weights 16 j .. 16 j + 15, codes_operand unpacks them in
-// order), one 8-byte load per row; step s (0, 1) feeds word 8 h + 2 g + s of
-// column row li and the 16 activation bytes at 128 h + 32 g + 16 s of token
-// row li.  Result lane l, register r holds (token 4 g + r, column li).
+// 256 h + 64 g .. +63, i.e. packed words 16 h + 4 g .. +3 of a row (word j
+// holds weights 16 j .. 16 j + 15, codes_operand unpacks them in order), one
+// 16-byte load per row, so a load instruction reads 64 contiguous bytes of
+// each of 16 rows (pieces of 128 weights, 8-byte loads and 32-byte runs,
+// measured 0.1-1.1 us slower on every shape this kernel runs); step s (0..3)
+// feeds word 16 h + 4 g + s of column row li and the 16 activation bytes at
+// 256 h + 64 g + 16 s of token row li.  Result lane l, register r holds
+// (token 4 g + r, column li).
 #include "bl_device.h"
 #include "bl_launch.h"
 
@@ -32,7 +35,7 @@ namespace bl {
 
 enum { KS_STORE = 0, KS_GATEUP = 1 };
 
-constexpr int kPiece = 128;  // K per piece
+constexpr int kPiece = 256;  // K per piece
 
 template <int NB, int TM, int TN, int W, int CPW, int EPI>
 __global__ __launch_bounds__(64 * W) void mfma_ksplit_kernel(
@@ -81,8 +84,9 @@ __global__ __launch_bounds__(64 * W) void mfma_ksplit_kernel(
   const buf_rsrc rb1 = make_buf_rsrc((NB == 2 ? W1 : W0) + n0 * wpr, (uint32_t)(nrows * wpr * 4));
 
   // ---- every load of the wave, piece by piece
-  u32x4 a_reg[CPW][TM][2];
-  uint32_t b_reg[CPW][NB][TN][2];
+  constexpr int NS = kPiece / 64;  // MFMA k-steps per piece
+  u32x4 a_reg[CPW][TM][NS];
+  u32x4 b_reg[CPW][NB][TN];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int64_t h = h0 + j;
@@ -90,14 +94,14 @@ __global__ __launch_bounds__(64 * W) void mfma_ksplit_kernel(
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int64_t k = kPiece * h + 32 * g + 16 * s;
+      for (int s = 0; s < NS; ++s) {
+        const int64_t k = kPiece * h + 16 * NS * g + 16 * s;
         const uint32_t off =
             live && k < Kp ? (uint32_t)((16 * tm + li) * Kp + k) : 0x80000000u;
         a_reg[j][tm][s] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
       }
     }
-    const int64_t word = 8 * h + 2 * g;
+    const int64_t word = (kPiece / 16) * h + NS * g;
 #pragma unroll
     for (int mat = 0; mat < NB; ++mat) {
 #pragma unroll
@@ -105,10 +109,7 @@ __global__ __launch_bounds__(64 * W) void mfma_ksplit_kernel(
         const uint32_t off = live && word < wpr
                                  ? (uint32_t)(((16 * tn + li) * wpr + word) * 4)
                                  : 0x80000000u;
-        const uint2 v = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_raw_buffer_load_b64(mat == 0 ? rb0 : rb1, off, 0, 0));
-        b_reg[j][mat][tn][0] = v.x;
-        b_reg[j][mat][tn][1] = v.y;
+        b_reg[j][mat][tn] = __builtin_amdgcn_raw_buffer_load_b128(mat == 0 ? rb0 : rb1, off, 0, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64 * W) void mfma_ksplit_kernel(
   for (int j = 0; j < CPW; ++j) {
     if (j < hn) {  // uniform over the wave
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < NS; ++s) {
 #pragma unroll
         for (int mat = 0; mat < NB; ++mat) {
 #pragma unroll
@@ -239,48 +240,44 @@ static int ks_ppw(int64_t Kp) {
 }
 
 // Pieces per wave held in registers: the smallest instance that covers Kp
-// (at most 8: 24 VGPRs of loads per piece for the gate/up tile).
-template <int NB, int TM, int TN, int EPI>
+// (at most 4: up to 80 VGPRs of loads per piece for the 64 x 32 gate/up tile).
+template <int NB, int TM, int TN, int EPI, int MAXC = 4>
 static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                              int64_t Kp, const uint32_t* W0, const float* s0, const uint32_t* W1,
                              const float* s1, int64_t N, float* Y, int32_t* acc_out,
                              float* gh_parts, int* nparts, hipStream_t s) {
   const int ppw = ks_ppw(Kp);
-#define BL_KS_GO(C)                                                                          \
-  if (ppw <= (C))                                                                            \
-  return ksplit_go<NB, TM, TN, kKsWaves, (C), EPI>(Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y,  \
-                                                   acc_out, gh_parts, nparts, ppw, s)
+#define BL_KS_GO(C)                                                                        \
+  if ((C) <= MAXC && ppw <= (C))                                                           \
+  return ksplit_go<NB, TM, TN, kKsWaves, ((C) <= MAXC ? (C) : 1), EPI>(                     \
+      Xq, xs, rs, M, Kp, W0, s0, W1, s1, N, Y, acc_out, gh_parts, nparts, ppw, s)
   BL_KS_GO(1);
   BL_KS_GO(2);
   BL_KS_GO(3);
   BL_KS_GO(4);
-  BL_KS_GO(5);
-  BL_KS_GO(6);
-  BL_KS_GO(7);
-  BL_KS_GO(8);
 #undef BL_KS_GO
   return hipErrorInvalidValue;
 }
 
 // Where this kernel measured faster than the kernels it replaces (same box,
-// bit-identical results):
-// - 17..64 tokens, plain products with long K, on 16 x 48 tiles: the 2B-class
-//   6912 -> 2560 layer at 17 / 32 / 64 tokens 9.4 / 10.3 / 10.1 us against
-//   10.3 / 11.1 / 10.8 for the 32 x 32 block-tile kernel (kernel trace), and
-//   faster still on 16 x 32 tiles where those fit one block per CU (below);
-// - 2..16 tokens, plain products with K <= 4096 and 4096..16384 columns, on
-//   16 x 32 tiles: 2560 -> 6912 at 2 / 8 / 16 tokens 4.3 / 4.9 / 5.3 us
-//   against 4.7 / 5.5 / 6.3 for the direct and streaming kernels (events);
-// - the FFN's gate/up at 17..32 tokens on 32 x 32 tiles of both matrices
-//   (2560 -> 2 x 6912: 8.9 / 9.5 us against 10.1 / 10.2).
+// bit-identical results, events around graph replays):
+// - 17..64 tokens, plain products with long K: the 2B-class 6912 -> 2560
+//   layer at 17 / 32 / 64 tokens 6.8 / 7.3 / 8.8 us against 9.4 / 9.7 / 9.9
+//   for the 32 x 32 block-tile kernel;
+// - 2..16 tokens, plain products with K <= 4096 and 4096..16384 columns:
+//   2560 -> 6912 at 2 / 8 / 16 tokens 4.1 / 4.7 / 5.0 us against 4.7 / 5.5 /
+//   6.3 for the direct and streaming kernels;
+// - the FFN's gate/up at 17..64 tokens: the block at 17 / 32 / 48 / 64
+//   tokens 22.7 / 24.4 / 26.8 / 29.0 us against 27.6 / 28.7 / 30.2 / 30.7
+//   with the block-tile kernel (both products).
 // Measured slower and left to the other kernels: 2560 -> 6912 at 17..64
-// tokens (7.2-8.3 against 6.7-8.2 us), 6912 -> 2560 at 8 and 16 tokens (5.9 /
-// 7.0 against 5.6 / 6.3 us), gate/up at 2..16 tokens (the FFN block 1.2-1.6 us
-// slower) and at 48..64 tokens (12.1-12.3 against 11.9-12.0 us).
+// tokens, 6912 -> 2560 at 2..16 tokens, gate/up at 2..16 tokens (the FFN
+// block 1.2-1.6 us slower), and the 100B-class layer (32-byte weight runs
+// per load instruction then; two to three times slower than streaming).
 bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (M < 2 || M > 64 || ks_ppw(Kp) > 8) return false;
-  if (nb == 2) return M >= 17 && M <= 32;
+  if (M < 2 || M > 64 || ks_ppw(Kp) > 4) return false;
+  if (nb == 2) return M >= 17;
   if (M <= 16) return Kp <= 4096 && N >= 4096 && N <= 16384;
   return Kp >= 4096;
 }
@@ -289,10 +286,10 @@ hipError_t launch_ksplit(const int8_t* Xq, const float* xs, const int32_t* rs, i
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  // 16 x 32 tiles while they fit one block per CU, else 16 x 48 (6912 -> 2560
-  // at 17 / 32 / 48 tokens 7.6 / 8.4 / 8.4 us on 16 x 32 tiles against 9.2 /
-  // 10.2 / 10.2 on 16 x 48; at 64 tokens, 320 blocks of 16 x 32, 12.7 against
-  // 10.3 us)
+  // 16 x 32 tiles while they fit one block per CU, else 16 x 48 (measured
+  // with pieces of 128: 6912 -> 2560 at 17 / 32 / 48 tokens 7.6 / 8.4 / 8.4 us
+  // on 16 x 32 tiles against 9.2 / 10.2 / 10.2 on 16 x 48; at 64 tokens, 320
+  // blocks of 16 x 32, 12.7 against 10.3 us)
   const int64_t nbm = (M + 15) / 16;
   if (nbm * ((N + 31) / 32) <= 256)
     return ksplit_cpw<1, 1, 2, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
@@ -306,6 +303,12 @@ hipError_t launch_ksplit_gateup(const int8_t* Xq, const float* xs, const int32_t
                                 const uint32_t* Wu, const float* su, int64_t N, float* H,
                                 float* gh_parts, int* nparts, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
+  // 32 x 32 tiles of both matrices up to 32 tokens, 64 x 32 above (the FFN
+  // at 48 / 64 tokens 26.8 / 29.0 us against 28.1 / 30.2 with the block-tile
+  // gate/up kernel)
+  if (M > 32 && ks_ppw(Kp) <= 2)  // 64 x 32 tiles: more pieces per wave spill
+    return ksplit_cpw<2, 4, 2, KS_GATEUP, 2>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
+                                          gh_parts, nparts, s);
   return ksplit_cpw<2, 2, 2, KS_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                         gh_parts, nparts, s);
 }

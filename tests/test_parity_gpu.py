@@ -425,6 +425,9 @@ def test_ffn_2b_subln(M):
                                          # waves of a block: 1 to 5 pieces per wave
                                          (32, 2560, 6912, False), (24, 1000, 3000, True),
                                          (17, 4100, 900, False), (31, 120, 70, False),
+                                         # 33..64 tokens: 64 x 32 tiles while K fits two
+                                         # pieces of 256 per wave, 32 x 32 tiles above
+                                         (48, 5000, 700, False), (64, 300, 4500, True),
                                          (100, 256, 520, False), (256, 512, 1024, False),
                                          (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
                                          (100, 256, 520, True),
