@@ -235,6 +235,7 @@ static hipError_t ksplit_go(const int8_t* Xq, const float* xs, const int32_t* rs
 }
 
 constexpr int kKsWaves = 8;      // waves per block
+constexpr int64_t kKsBlocks = 256;  // blocks that fill the 256 CUs once
 static int ks_ppw(int64_t Kp) {
   return (int)(((Kp + kPiece - 1) / kPiece + kKsWaves - 1) / kKsWaves);
 }
@@ -261,41 +262,51 @@ static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* r
 
 // Where this kernel measured faster than the kernels it replaces (same box,
 // bit-identical results, events around graph replays):
-// - 17..64 tokens, plain products with long K: the 2B-class 6912 -> 2560
-//   layer at 17 / 32 / 64 tokens 6.8 / 7.3 / 8.8 us against 9.4 / 9.7 / 9.9
-//   for the 32 x 32 block-tile kernel;
+// - 17..64 tokens, plain products: 6912 -> 2560 at 17 / 32 / 64 tokens 6.8 /
+//   7.3 / 8.8 us against 9.4 / 9.7 / 9.9 for the 32 x 32 block-tile kernel,
+//   2560 -> 6912 at 17 / 32 / 64 tokens 6.1 / 6.2 / 7.7 against 6.2 / 6.4 / 8.4;
 // - 2..16 tokens, plain products with K <= 4096 and 4096..16384 columns:
-//   2560 -> 6912 at 2 / 8 / 16 tokens 4.1 / 4.7 / 5.0 us against 4.7 / 5.5 /
-//   6.3 for the direct and streaming kernels;
+//   2560 -> 6912 at 2 / 8 / 16 tokens 4.1 / 4.7 / 5.1 us against 4.7 / 5.5 /
+//   6.3 for the direct and streaming kernels; at 2 tokens with longer K too
+//   (6912 -> 2560: 4.5 against 5.0 us; at 4 and 8 tokens about even alone but
+//   the FFN block, whose down projection this is, 0.2 / 0.5 us slower, and at
+//   16 tokens 6.7 against 6.3 us, so from 3 tokens on the direct kernel);
 // - the FFN's gate/up at 17..64 tokens: the block at 17 / 32 / 48 / 64
 //   tokens 22.7 / 24.4 / 26.8 / 29.0 us against 27.6 / 28.7 / 30.2 / 30.7
 //   with the block-tile kernel (both products).
-// Measured slower and left to the other kernels: 2560 -> 6912 at 17..64
-// tokens, 6912 -> 2560 at 2..16 tokens, gate/up at 2..16 tokens (the FFN
-// block 1.2-1.6 us slower), and the 100B-class layer (32-byte weight runs
-// per load instruction then; two to three times slower than streaming).
+// Measured slower and left to the other kernels: gate/up at 2..16 tokens (the
+// FFN block 0.4-1.6 us slower), and the 100B-class layer (two to three times
+// slower than the streaming kernel with pieces of 128).  Layers of more than
+// 16384 or fewer than 2048 columns were not measured and stay where they were.
 bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (M < 2 || M > 64 || ks_ppw(Kp) > 4) return false;
+  if (M < 2 || M > 64 || ks_ppw(Kp) > 4 || N < 2048 || N > 16384) return false;
   if (nb == 2) return M >= 17;
-  if (M <= 16) return Kp <= 4096 && N >= 4096 && N <= 16384;
-  return Kp >= 4096;
+  if (M == 2) return true;
+  if (M <= 16) return Kp <= 4096 && N >= 4096;
+  return true;
 }
 
+// Tiles: the narrowest of 16 x 16, 16 x 32, 16 x 48, 16 x 64 that gives at
+// most one block per CU, else 32 x 64.  (With pieces of 128 weights, 16 x 32
+// against 16 x 48 tiles for 6912 -> 2560 at 17 / 32 / 48 tokens: 7.6 / 8.4 /
+// 8.4 against 9.2 / 10.2 / 10.2 us; at 64 tokens, 320 blocks of 16 x 32, 12.7
+// against 10.3 us.)
 hipError_t launch_ksplit(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  // 16 x 32 tiles while they fit one block per CU, else 16 x 48 (measured
-  // with pieces of 128: 6912 -> 2560 at 17 / 32 / 48 tokens 7.6 / 8.4 / 8.4 us
-  // on 16 x 32 tiles against 9.2 / 10.2 / 10.2 on 16 x 48; at 64 tokens, 320
-  // blocks of 16 x 32, 12.7 against 10.3 us)
   const int64_t nbm = (M + 15) / 16;
-  if (nbm * ((N + 31) / 32) <= 256)
-    return ksplit_cpw<1, 1, 2, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y,
-                                         acc_out, nullptr, nullptr, s);
-  return ksplit_cpw<1, 1, 3, KS_STORE>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, N, Y, acc_out,
-                                       nullptr, nullptr, s);
+#define BL_KS_TILE(TM_, TN_, MAXC_)                                                          \
+  return ksplit_cpw<1, TM_, TN_, KS_STORE, MAXC_>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, \
+                                                  N, Y, acc_out, nullptr, nullptr, s)
+  if (nbm * ((N + 15) / 16) <= kKsBlocks) BL_KS_TILE(1, 1, 4);
+  if (nbm * ((N + 31) / 32) <= kKsBlocks) BL_KS_TILE(1, 2, 4);
+  if (nbm * ((N + 47) / 48) <= kKsBlocks) BL_KS_TILE(1, 3, 4);
+  if (nbm * ((N + 63) / 64) <= kKsBlocks) BL_KS_TILE(1, 4, 4);
+  if (((M + 31) / 32) * ((N + 63) / 64) <= kKsBlocks && ks_ppw(Kp) <= 2) BL_KS_TILE(2, 4, 2);
+  BL_KS_TILE(1, 3, 4);
+#undef BL_KS_TILE
 }
 
 hipError_t launch_ksplit_gateup(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,

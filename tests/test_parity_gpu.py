@@ -127,8 +127,12 @@ def test_single_layer_512_to_400_all_kernels():
     # 17..64 tokens with long K on the kernel that splits K over the waves of a
     # block: ragged 16-token and 48-column tiles, the most pieces per wave (8)
     (17, 6912, 100), (33, 8192, 2600), (64, 4096, 2561), (40, 8100, 47),
-    # 2..16 tokens with K <= 4096 and 4096..16384 columns on the same kernel
+    # 2..16 tokens with K <= 4096 and 4096..16384 columns on the same kernel,
+    # 2 tokens with any K it takes; 17..64 tokens with short K; every tile
+    # shape (16 x 16 .. 16 x 64, 32 x 64) and the fallback past 256 blocks
     (2, 2560, 6912), (9, 4096, 4097), (16, 1000, 16384), (5, 65, 5000),
+    (2, 6912, 2560), (2, 8192, 2048), (5, 5000, 3001), (17, 2560, 6912), (64, 2560, 6912),
+    (50, 1000, 9000), (33, 3000, 2048),
     # one token, packed matrix >= 16 MiB (the streaming GEMV), ragged K and odd N
     (1, 5000, 13301), (1, 4000, 17001), (1, 8192, 16385), (1, 8192, 8192), (1, 8192, 12001),
     (1, 4096, 40000),
