@@ -158,8 +158,10 @@ int bitlinear_quant_act(const void *X, int dtype, int64_t M, int64_t K, int8_t *
  *  Y        [M][N] float32, device, 4-byte aligned, written.
  *  acc_out  [M][N] int32, device, or NULL; when given, the exact integer
  *           accumulators are written too (for inspection).
- *  The kernel is chosen by M (1: GEMV; <= 64: skinny MFMA; else tiled MFMA
- *  GEMM); all give identical bits.
+ *  The kernel is chosen by the shape (1 token: GEMV; up to 64 tokens: the
+ *  skinny MFMA kernels; up to 512 tokens on layers of 2048..16384 outputs:
+ *  mostly the MFMA kernel that splits K over the waves of a block; else the
+ *  tiled MFMA GEMM); all give identical bits.
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EHIP.
  */
 int bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
@@ -227,7 +229,8 @@ int bitlinear_forward_a48(const int8_t *Xq4, const float *x4_scale, const int32_
 /* bitlinear_forward with the kernel chosen by the caller (for cross-checks
  * and timing): BL_KERNEL_AUTO as bitlinear_forward; BL_KERNEL_GEMV needs
  * M == 1; BL_KERNEL_SKINNY needs M <= 64 (one MFMA tile row of 16/32/64
- * tokens); BL_KERNEL_TILED is the 128 x 128 tiled MFMA GEMM for any M.
+ * tokens, any of the skinny kernels); BL_KERNEL_TILED is the 128 x 256
+ * tiled MFMA GEMM for any M.
  * Errors as bitlinear_forward, plus BL_ESHAPE when M does not fit the
  * chosen kernel and BL_EINVAL for an unknown kernel id. */
 enum { BL_KERNEL_AUTO = 0, BL_KERNEL_GEMV = 1, BL_KERNEL_SKINNY = 2, BL_KERNEL_TILED = 3 };

@@ -473,8 +473,8 @@ hipError_t launch_forward_a48(const int8_t* x4, const float* g4, const int32_t* 
     e = launch_mfma(x4, g4, rs4, 2 * M, K, Wp, ws, N, nullptr, acc, false, s);
   } else {
     // two products with their accumulators kept
-    e = launch_mfma(x4, g4, rs4, M, K, Wp, ws, N, Y, acc, M > 64, s);
-    if (e == hipSuccess) e = launch_mfma(x8, g8, rs8, M, K, Wp, ws, N, Y, acc + M * N, M > 64, s);
+    e = launch_mfma(x4, g4, rs4, M, K, Wp, ws, N, Y, acc, false, s);
+    if (e == hipSuccess) e = launch_mfma(x8, g8, rs8, M, K, Wp, ws, N, Y, acc + M * N, false, s);
   }
   if (e != hipSuccess) return e;
   const int64_t total = M * N;

@@ -140,8 +140,12 @@ int bitlinear_forward_kernel(const int8_t* Xq, const float* x_scale, const int32
   int st = check_forward(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y);
   if (st != BL_OK) return st;
   if (acc_out && !aligned(acc_out, 4)) return BL_EALIGN;
-  if (kernel == BL_KERNEL_AUTO) kernel = (M == 1) ? BL_KERNEL_GEMV : (M <= 64 ? BL_KERNEL_SKINNY : BL_KERNEL_TILED);
   hipStream_t s = as_stream(stream);
+  if (kernel == BL_KERNEL_AUTO) {
+    if (M == 1) return hip_status(bl::launch_gemv(Xq, x_scale, x_rowsum, K, Wp, w_scale, N, Y, acc_out, s));
+    return hip_status(
+        bl::launch_mfma(Xq, x_scale, x_rowsum, M, K, Wp, w_scale, N, Y, acc_out, false, s));
+  }
   switch (kernel) {
     case BL_KERNEL_GEMV:
       if (M != 1) return BL_ESHAPE;
@@ -247,7 +251,7 @@ int bitlinear_forward_fused(const void* X, int dtype, int64_t M, int64_t K, cons
   hipError_t e = bl::launch_act_quant(X, bf16, M, K, xq, xs, rs, nullptr, 0, s);
   if (e != hipSuccess) return BL_EHIP;
   if (M == 1) return hip_status(bl::launch_gemv(xq, xs, rs, K, Wp, w_scale, N, Y, nullptr, s));
-  return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
+  return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, false, s));
 }
 
 size_t bitlinear_fused_norm_workspace_bytes(int64_t M, int64_t K) {
@@ -280,7 +284,7 @@ int bitlinear_forward_fused_norm(const void* X, int dtype, int64_t M, int64_t K,
   hipError_t e = bl::launch_rmsnorm_quant(X, bf16, M, K, norm_w, norm_eps, xn, xq, xs, rs, s);
   if (e != hipSuccess) return BL_EHIP;
   if (M == 1) return hip_status(bl::launch_gemv(xq, xs, rs, K, Wp, w_scale, N, Y, nullptr, s));
-  return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, M > 64, s));
+  return hip_status(bl::launch_mfma(xq, xs, rs, M, K, Wp, w_scale, N, Y, nullptr, false, s));
 }
 
 size_t bitnet_ffn_workspace_layout(int64_t M, int64_t D, int64_t F, size_t* off) {
@@ -368,7 +372,7 @@ static int ffn_run(const void* H, int dtype, int64_t M, int64_t D, int64_t F,
   if (M == 1)
     e = bl::launch_gemv(qh, gh, rsh, F, Wd, sd, D, Y, nullptr, s);
   else
-    e = bl::launch_mfma(qh, gh, rsh, M, F, Wd, sd, D, Y, nullptr, M > 64, s);
+    e = bl::launch_mfma(qh, gh, rsh, M, F, Wd, sd, D, Y, nullptr, false, s);
   return hip_status(e);
 }
 

@@ -83,8 +83,9 @@ hipError_t launch_gemv_norm(const float* X, int64_t K, const float* norm_w, floa
                             float* xn_out, int8_t* xq_out, float* xs_out, int32_t* rs_out,
                             hipStream_t s);
 
-// Y = dequant(Xq . T^T) on MFMA: skinny (M <= 64, tiled == false) or the
-// 128 x 128 tiled kernel.
+// Y = dequant(Xq . T^T) on MFMA.  tiled == true: the 128 x 256 tiled
+// kernel; false: the kernel the shape measured fastest on (the skinny
+// kernels up to 64 tokens, the K-split kernel where ksplit_ok, else tiled).
 hipError_t launch_mfma(const int8_t* Xq, const float* x_scale, const int32_t* rowsum, int64_t M,
                        int64_t K, const uint32_t* Wp, const float* w_scale, int64_t N, float* Y,
                        int32_t* acc_out, bool tiled, hipStream_t s);

@@ -702,9 +702,10 @@ hipError_t launch_mfma(const int8_t* Xq, const float* xs, const int32_t* rs, int
                        const uint32_t* Wp, const float* ws, int64_t N, float* Y, int32_t* acc_out,
                        bool tiled, hipStream_t s) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  if (tiled || M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
+  if (tiled) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   // K split over the waves of a block, where that measured faster (ksplit_ok)
   if (ksplit_ok(M, K, N, 1)) return launch_ksplit(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
+  if (M > 64) return launch_mfma32(Xq, xs, rs, M, K, Wp, ws, N, Y, acc_out, s);
   // large layers: the streaming kernel with 7- or 8-wave blocks (activations
   // staged in phases when they do not fit), 18.5 us against the direct
   // kernel's 39.5 us on the 100B-class layer at 16 tokens

@@ -280,6 +280,14 @@ static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* r
 // 16384 or fewer than 2048 columns were not measured and stay where they were.
 bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
   const int64_t Kp = (K + 63) / 64 * 64;
+  // 65..512 tokens, plain products: where the 128 x 256 tiled GEMM has few
+  // tiles (same box, events; 2560 -> 6912 at 65 / 128 / 192 / 256 / 512
+  // tokens 10.7 / 11.3 / 15.9 / 20.5 / 38.5 us against 23.0 / 20.9 / 22.5 /
+  // 20.6 / 21.2 for the tiled kernel; 6912 -> 2560 at 65 / 128 / 256 / 512
+  // tokens 8.9 / 15.6 / 22.0 / 36.2 against 44.4 / 42.3 / 41.8 / 42.2): up to
+  // 192 tokens, and up to 512 with K of 4096 or more
+  if (nb == 1 && M > 64)
+    return M <= 512 && (M <= 192 || Kp >= 4096) && ks_ppw(Kp) <= 4 && N >= 2048 && N <= 16384;
   if (M < 2 || M > 64 || ks_ppw(Kp) > 4 || N < 2048 || N > 16384) return false;
   if (nb == 2) return M >= 17;
   if (M == 2) return true;
@@ -300,6 +308,30 @@ hipError_t launch_ksplit(const int8_t* Xq, const float* xs, const int32_t* rs, i
 #define BL_KS_TILE(TM_, TN_, MAXC_)                                                          \
   return ksplit_cpw<1, TM_, TN_, KS_STORE, MAXC_>(Xq, xs, rs, M, Kp, Wp, ws, nullptr, nullptr, \
                                                   N, Y, acc_out, nullptr, nullptr, s)
+  if (M > 64) {
+    // the tile (up to 64 x 64, within the register budget of its pieces per
+    // wave) that moves the fewest bytes through the busiest CU
+    struct Cand { int tm, tn, maxc; };
+    static const Cand cands[] = {{1, 2, 4}, {1, 4, 4}, {2, 2, 4}, {2, 4, 2}, {4, 2, 2}, {4, 4, 2}};
+    const int ppw = ks_ppw(Kp);
+    int best = -1;
+    int64_t bb = 0;
+    for (int i = 0; i < 6; ++i) {
+      if (ppw > cands[i].maxc) continue;
+      const int64_t bm = 16 * cands[i].tm, bn = 16 * cands[i].tn;
+      const int64_t blocks = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+      const int64_t bytes = (blocks + kKsBlocks - 1) / kKsBlocks * (bm * Kp + bn * (Kp / 4));
+      if (best < 0 || bytes < bb) best = i, bb = bytes;
+    }
+    switch (best) {
+      case 0: BL_KS_TILE(1, 2, 4);
+      case 1: BL_KS_TILE(1, 4, 4);
+      case 2: BL_KS_TILE(2, 2, 4);
+      case 3: BL_KS_TILE(2, 4, 2);
+      case 4: BL_KS_TILE(4, 2, 2);
+      default: BL_KS_TILE(4, 4, 2);
+    }
+  }
   if (nbm * ((N + 15) / 16) <= kKsBlocks) BL_KS_TILE(1, 1, 4);
   if (nbm * ((N + 31) / 32) <= kKsBlocks) BL_KS_TILE(1, 2, 4);
   if (nbm * ((N + 47) / 48) <= kKsBlocks) BL_KS_TILE(1, 3, 4);
