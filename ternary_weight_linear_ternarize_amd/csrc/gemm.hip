@@ -788,7 +788,7 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
   // 17 <= M <= 64: 32 x 32 block tiles with 2 chunks of loads in flight
   // (the FFN at 64 tokens 35.2 us against 38.2 with 64 x 16 tiles and one
   // chunk in flight, at 32 tokens 28.7 against 33.7)
-  // 17..64 tokens: K split over the waves of a block
+  // 17..192 tokens: K split over the waves of a block (ksplit_ok)
   if (ksplit_ok(M, K, N, 2))
     return launch_ksplit_gateup(Xq, xs, rs, M, K, Wg, sg, Wu, su, N, H, gh_parts, nparts, s);
   if (M <= 64)

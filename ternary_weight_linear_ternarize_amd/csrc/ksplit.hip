@@ -286,6 +286,11 @@ bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
   // 20.6 / 21.2 for the tiled kernel; 6912 -> 2560 at 65 / 128 / 256 / 512
   // tokens 8.9 / 15.6 / 22.0 / 36.2 against 44.4 / 42.3 / 41.8 / 42.2): up to
   // 192 tokens, and up to 512 with K of 4096 or more
+  // the FFN's gate/up past 64 tokens: the block at 65 / 96 / 128 / 192 tokens
+  // 35.8 / 39.4 / 47.5 / 57.8 us against 51.9 / 53.8 / 60.7 / 61.1 with the
+  // 128 x 128 block-tile gate/up (at 256 / 512 tokens 74.5 / 115.5 against
+  // 70.2 / 85.1, left to it)
+  if (nb == 2 && M > 64) return M <= 192 && ks_ppw(Kp) <= 4 && N >= 2048 && N <= 16384;
   if (nb == 1 && M > 64)
     return M <= 512 && (M <= 192 || Kp >= 4096) && ks_ppw(Kp) <= 4 && N >= 2048 && N <= 16384;
   if (M < 2 || M > 64 || ks_ppw(Kp) > 4 || N < 2048 || N > 16384) return false;

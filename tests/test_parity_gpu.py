@@ -435,6 +435,10 @@ def test_ffn_2b_subln(M):
                                          # 33..64 tokens: 64 x 32 tiles while K fits two
                                          # pieces of 256 per wave, 32 x 32 tiles above
                                          (48, 5000, 700, False), (64, 300, 4500, True),
+                                         # 65..192 tokens: gate/up on the same kernel;
+                                         # 200 tokens past its range
+                                         (100, 2560, 6912, False), (192, 3000, 2500, True),
+                                         (200, 1000, 2100, False),
                                          (100, 256, 520, False), (256, 512, 1024, False),
                                          (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
                                          (100, 256, 520, True),
