@@ -159,9 +159,9 @@ int bitlinear_quant_act(const void *X, int dtype, int64_t M, int64_t K, int8_t *
  *  acc_out  [M][N] int32, device, or NULL; when given, the exact integer
  *           accumulators are written too (for inspection).
  *  The kernel is chosen by the shape (1 token: GEMV; up to 64 tokens: the
- *  skinny MFMA kernels; up to 512 tokens on layers of 2048..16384 outputs:
- *  mostly the MFMA kernel that splits K over the waves of a block; else the
- *  tiled MFMA GEMM); all give identical bits.
+ *  skinny MFMA kernels; up to 192 tokens (384 with K >= 4096) on layers of
+ *  2048..16384 outputs: the MFMA kernel that splits K over the waves of a
+ *  block; else the tiled MFMA GEMM); all give identical bits.
  *  Errors: BL_EINVAL, BL_ESHAPE, BL_EALIGN, BL_EHIP.
  */
 int bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,

@@ -802,21 +802,34 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
 
 namespace bl {
 
-hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
-                         int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
-                         int32_t* acc_out, hipStream_t s) {
-  constexpr int TM = 4, TN = 2, WM = 1, WN = 4;
+template <int TM, int TN, int WM, int WN>
+static hipError_t tiled_go(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                           int64_t Kp, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                           int32_t* acc_out, hipStream_t s) {
   using G = TiledGemm<TM, TN, WM, WN>;
   static bool once = ((void)hipFuncSetAttribute(
                           reinterpret_cast<const void*>(tiled_gemm_kernel<TM, TN, WM, WN>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS),
                       true);
   (void)once;
-  const int64_t Kp = (K + 63) / 64 * 64;
   const int64_t nbm = (M + G::BM - 1) / G::BM, nbn = (N + G::BN - 1) / G::BN;
   hipLaunchKernelGGL((tiled_gemm_kernel<TM, TN, WM, WN>), dim3((unsigned)(nbm * nbn)), dim3(256),
                      G::LDS, s, Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, (int)nbm);
   return hipGetLastError();
+}
+
+hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                         int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
+                         int32_t* acc_out, hipStream_t s) {
+  const int64_t Kp = (K + 63) / 64 * 64;
+  // 128 x 128 tiles while those fill the CUs at most once, 128 x 256 above
+  // (same box, events: 2560 -> 6912 at 256 / 512 tokens 18.1 / 19.2 against
+  // 20.7 / 21.3 us, 6912 -> 2560 at 768 / 1024 / 1536 tokens 33.7 / 33.6 /
+  // 35.6 against 43.5 / 43.3 / 43.9 us; 2560 -> 6912 at 768 / 1024 tokens,
+  // 324 / 432 tiles of 128 x 128, 25.5 / 27.6 against 22.9 / 25.3 us)
+  if (((M + 127) / 128) * ((N + 127) / 128) <= 256)
+    return tiled_go<4, 1, 1, 4>(Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, s);
+  return tiled_go<4, 2, 1, 4>(Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, s);
 }
 
 }  // namespace bl

@@ -48,8 +48,9 @@ __device__ __forceinline__ float dequant_f64(int a, float s) {
 // passes of as many rows as fit, and stores whole 1 KB row segments, 16
 // bytes per lane (non-temporal: Y is not read back here); against one
 // 4-byte store per register (two 128-byte row segments) this takes 37-38 us
-// instead of 42-43 for 2048 x 2560 x 6912.  Edge tiles, and calls that also
-// want the int32 accumulators, store from the registers directly.
+// instead of 42-43 for 2048 x 2560 x 6912.  Edge tiles, tiles narrower than
+// 256 columns, and calls that also want the int32 accumulators store from
+// the registers directly.
 //
 // Out-of-range rows and the K tail read as zero through the buffer
 // resources' bounds, so the main loop has no per-lane range checks.  Block b
@@ -201,13 +202,12 @@ __global__ __launch_bounds__(256, MINB) void tiled_gemm_kernel(
     if (c + 1 < nchunks) step(c + 1, 1, bB, bA);
   }
 
-  if (mrows == BM && nrows == BN && !acc_out) {
+  if (BN % 256 == 0 && mrows == BM && nrows == BN && !acc_out) {
     // RP rows of the tile per pass through the two activation buffers
-    static_assert(BN % 256 == 0, "a row segment is a multiple of 64 lanes x 16 bytes");
     constexpr int RP = (2 * ABYTES) / (BN * 4) >= BM ? BM : BM / 2;
     static_assert(RP * BN * 4 <= 2 * ABYTES && BM % RP == 0 && RP % 32 == 0 && RP % 4 == 0,
                   "epilogue passes");
-    constexpr int SEG = BN / 256;  // 1 KB segments per row
+    constexpr int SEG = BN / 256 > 0 ? BN / 256 : 1;  // 1 KB segments per row
     float* ep = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int p = 0; p < BM / RP; ++p) {

@@ -280,19 +280,21 @@ static hipError_t ksplit_cpw(const int8_t* Xq, const float* xs, const int32_t* r
 // 16384 or fewer than 2048 columns were not measured and stay where they were.
 bool ksplit_ok(int64_t M, int64_t K, int64_t N, int nb) {
   const int64_t Kp = (K + 63) / 64 * 64;
-  // 65..512 tokens, plain products: where the 128 x 256 tiled GEMM has few
-  // tiles (same box, events; 2560 -> 6912 at 65 / 128 / 192 / 256 / 512
-  // tokens 10.7 / 11.3 / 15.9 / 20.5 / 38.5 us against 23.0 / 20.9 / 22.5 /
-  // 20.6 / 21.2 for the tiled kernel; 6912 -> 2560 at 65 / 128 / 256 / 512
-  // tokens 8.9 / 15.6 / 22.0 / 36.2 against 44.4 / 42.3 / 41.8 / 42.2): up to
-  // 192 tokens, and up to 512 with K of 4096 or more
   // the FFN's gate/up past 64 tokens: the block at 65 / 96 / 128 / 192 tokens
   // 35.8 / 39.4 / 47.5 / 57.8 us against 51.9 / 53.8 / 60.7 / 61.1 with the
   // 128 x 128 block-tile gate/up (at 256 / 512 tokens 74.5 / 115.5 against
   // 70.2 / 85.1, left to it)
   if (nb == 2 && M > 64) return M <= 192 && ks_ppw(Kp) <= 4 && N >= 2048 && N <= 16384;
+  // 65..384 tokens, plain products: where the tiled GEMM has few tiles (same
+  // box, events; 2560 -> 6912 at 65 / 128 / 192 / 256 tokens 10.7 / 11.3 /
+  // 15.9 / 20.5 us against 23.0 / 20.9 / 22.5 / 20.6 on 128 x 256 tiles and
+  // 18.1 at 256 on 128 x 128; 6912 -> 2560 at 65 / 128 / 256 / 384 / 512
+  // tokens 8.9 / 15.6 / 22.0 / 29.0 / 36.0 against 44.4 / 42.3 / 41.8 / 41.8 /
+  // 42.2 on 128 x 256 tiles and 33.7 on 128 x 128 at 768): up to 192 tokens,
+  // and up to 384 with K of 4096 or more
   if (nb == 1 && M > 64)
-    return M <= 512 && (M <= 192 || Kp >= 4096) && ks_ppw(Kp) <= 4 && N >= 2048 && N <= 16384;
+    return (M <= 192 || (M <= 384 && Kp >= 4096)) && ks_ppw(Kp) <= 4 && N >= 2048 &&
+           N <= 16384;
   if (M < 2 || M > 64 || ks_ppw(Kp) > 4 || N < 2048 || N > 16384) return false;
   if (nb == 2) return M >= 17;
   if (M == 2) return true;

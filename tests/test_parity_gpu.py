@@ -133,9 +133,12 @@ def test_single_layer_512_to_400_all_kernels():
     (2, 2560, 6912), (9, 4096, 4097), (16, 1000, 16384), (5, 65, 5000),
     (2, 6912, 2560), (2, 8192, 2048), (5, 5000, 3001), (17, 2560, 6912), (64, 2560, 6912),
     (50, 1000, 9000), (33, 3000, 2048),
-    # 65..512 tokens on the K-split kernel (tiles up to 64 x 64, chosen by the
+    # 65..384 tokens on the K-split kernel (tiles up to 64 x 64, chosen by the
     # bytes through the busiest CU) and past its range on the tiled GEMM
-    (65, 2560, 6912), (128, 6912, 2560), (200, 5000, 3000), (511, 4500, 2049), (300, 2560, 4096),
+    (65, 2560, 6912), (128, 6912, 2560), (200, 5000, 3000), (384, 4500, 2049), (511, 4500, 2049),
+    (300, 2560, 4096),
+    # the tiled GEMM on 128 x 128 tiles (at most 256 of them) and on 128 x 256
+    (777, 6912, 2560), (1100, 700, 2000), (520, 2560, 6912),
     # one token, packed matrix >= 16 MiB (the streaming GEMV), ragged K and odd N
     (1, 5000, 13301), (1, 4000, 17001), (1, 8192, 16385), (1, 8192, 8192), (1, 8192, 12001),
     (1, 4096, 40000),
