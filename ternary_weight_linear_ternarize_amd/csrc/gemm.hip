@@ -37,6 +37,10 @@ enum { MF_STORE = 0, MF_GATEUP = 1, MF_A48 = 2 };
 hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
                          int64_t K, const uint32_t* Wp, const float* ws, int64_t N, float* Y,
                          int32_t* acc_out, hipStream_t s);
+hipError_t launch_tiled_gateup(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                               int64_t K, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
+                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
+                               hipStream_t s);
 
 constexpr int kChunk = 256;         // K per chunk
 constexpr int kLdsPitch = 256 + 16; // bytes per staged activation row
@@ -794,6 +798,11 @@ hipError_t launch_mfma_gateup(const int8_t* Xq, const float* xs, const int32_t* 
   if (M <= 64)
     return mfma_launch<1, 1, 2, 2, MF_GATEUP, 2>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                                  gh_parts, nparts, s);
+  // the tiled GEMM with both matrices once its 128 x 128 tiles fill the CUs
+  // more than once (the FFN block at 1024 / 2048 tokens 121.6 / 207.2 ->
+  // 105.3 / 168.9 us; at 193 / 256 / 512 tokens 1-2 us slower, so not there)
+  if (((M + 127) / 128) * ((N + 127) / 128) > 256)
+    return launch_tiled_gateup(Xq, xs, rs, M, K, Wg, sg, Wu, su, N, H, gh_parts, nparts, s);
   return mfma_launch<4, 4, 2, 2, MF_GATEUP>(Xq, xs, rs, M, Kp, Wg, sg, Wu, su, N, H, nullptr,
                                             gh_parts, nparts, s);
 }
@@ -830,6 +839,28 @@ hipError_t launch_mfma32(const int8_t* Xq, const float* xs, const int32_t* rs, i
   if (((M + 127) / 128) * ((N + 127) / 128) <= 256)
     return tiled_go<4, 1, 1, 4>(Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, s);
   return tiled_go<4, 2, 1, 4>(Xq, xs, rs, M, Kp, Wp, ws, N, Y, acc_out, s);
+}
+
+// The FFN's gate/up past 192 tokens on the tiled GEMM: 128 x 128 tiles of
+// both matrices (the register count of one matrix's 128 x 256 tile).
+hipError_t launch_tiled_gateup(const int8_t* Xq, const float* xs, const int32_t* rs, int64_t M,
+                               int64_t K, const uint32_t* Wg, const float* sg, const uint32_t* Wu,
+                               const float* su, int64_t N, float* H, float* gh_parts, int* nparts,
+                               hipStream_t s) {
+  constexpr int TM = 4, TN = 1, WM = 1, WN = 4;
+  using G = TiledGemm<TM, TN, WM, WN, 2>;
+  static bool once = ((void)hipFuncSetAttribute(
+                          reinterpret_cast<const void*>(tiled_gemm_kernel<TM, TN, WM, WN, 2, 2>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS),
+                      true);
+  (void)once;
+  const int64_t Kp = (K + 63) / 64 * 64;
+  const int64_t nbm = (M + G::BM - 1) / G::BM, nbn = (N + G::BN - 1) / G::BN;
+  if (nparts) *nparts = (int)nbn;
+  hipLaunchKernelGGL((tiled_gemm_kernel<TM, TN, WM, WN, 2, 2>), dim3((unsigned)(nbm * nbn)),
+                     dim3(256), G::LDS, s, Xq, xs, rs, M, Kp, Wg, sg, N, H, nullptr, (int)nbm, Wu,
+                     su, gh_parts);
+  return hipGetLastError();
 }
 
 }  // namespace bl

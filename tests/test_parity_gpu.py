@@ -441,7 +441,8 @@ def test_ffn_2b_subln(M):
                                          # 65..192 tokens: gate/up on the same kernel;
                                          # 200 tokens past its range
                                          (100, 2560, 6912, False), (192, 3000, 2500, True),
-                                         (200, 1000, 2100, False),
+                                         (200, 1000, 2100, False), (300, 700, 1000, True),
+                                         (513, 2560, 6912, False), (700, 300, 5000, True),
                                          (100, 256, 520, False), (256, 512, 1024, False),
                                          (1, 300, 9000, True), (5, 64, 130, True), (40, 1000, 3000, True),
                                          (100, 256, 520, True),
