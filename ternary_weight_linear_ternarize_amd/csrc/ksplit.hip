@@ -1,4 +1,4 @@
-// Ternary x int8 product for 2..64 tokens with K split over every wave of
+// Ternary x int8 product for 2..384 tokens with K split over every wave of
 // the block and every load of a wave issued before the first MFMA.
 //
 // youngju.dev "BitNet論文分析", section "BitNet b1.58": the integer product is
@@ -9,7 +9,9 @@
 //
 // At these token counts a layer moves a few MB (the 2B-class FFN at 64
 // tokens: 8.8 MB of gate/up weights, 160 KB of activation codes), so its time
-// is set by how many bytes each CU has in flight, not by the matrix cores.
+// is set by how many bytes each CU has in flight, not by the matrix cores;
+// chains of dependent K chunks (one per 256 weights in the block-tile and
+// tiled kernels) are what it removes.
 // A block owns a BM x BN output tile (BM = 16 TM tokens, BN = 16 TN columns
 // of each of NB weight matrices) and its W waves split K between them: K is
 // cut into pieces of 256, wave w takes pieces [w ppw, (w + 1) ppw), and all
@@ -24,7 +26,7 @@
 // holds weights 16 j .. 16 j + 15, codes_operand unpacks them in order), one
 // 16-byte load per row, so a load instruction reads 64 contiguous bytes of
 // each of 16 rows (pieces of 128 weights, 8-byte loads and 32-byte runs,
-// measured 0.1-1.1 us slower on every shape this kernel runs); step s (0..3)
+// measured 0.1-1.4 us slower on every shape this kernel runs); step s (0..3)
 // feeds word 16 h + 4 g + s of column row li and the 16 activation bytes at
 // 256 h + 64 g + 16 s of token row li.  Result lane l, register r holds
 // (token 4 g + r, column li).
