@@ -485,14 +485,15 @@ def extra_workloads(torch, B, synth, dev):
     del copies, Y, X, q, Wp
     torch.cuda.empty_cache()
 
-    # skinny products on the 2B-class shapes: 2..64 tokens from int8 codes,
+    # skinny and medium-batch products on the 2B-class shapes: 2..512 tokens
+    # from int8 codes,
     # rotating weight copies (> 512 MB)
     d2 = synth.decode_2b()
     for name, K, N in (("W_up", 2560, 6912), ("W_down", 6912, 2560)):
         Wp, sc = B.bitlinear_pack(torch.from_numpy(d2[name]).to(dev))
         ncp = max(2, int(np.ceil(600e6 / (Wp.numel() * 4))))
         cps = [Wp.clone() for _ in range(ncp)]
-        for M in (2, 8, 16, 32, 64):
+        for M in (2, 8, 16, 32, 64, 128, 512):
             q = B.bitlinear_quant_act(torch.from_numpy(synth.normal(9, M, (M, K))).to(dev))
             Y = torch.empty((M, N), dtype=torch.float32, device=dev)
             ms = graph_time_per_launch(
@@ -500,7 +501,8 @@ def extra_workloads(torch, B, synth, dev):
                 ncp, 5, torch)
             res[f"forward_{K}x{N}_M{M}"] = {
                 "avg_us": round(ms * 1e3, 2),
-                "weight_GBps": round(Wp.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
+                "weight_GBps": round(Wp.numel() * 4 / (ms * 1e-3) / 1e9, 1),
+                "TOPS": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
         del cps, Wp
     del d2
     torch.cuda.empty_cache()
